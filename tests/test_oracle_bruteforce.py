@@ -1,0 +1,106 @@
+"""Oracle vs a push-style pure-Python brute force on tiny random inputs,
+including duplicate ids, out-of-range / negative ids, ragged counts,
+P = 1 and k = 1.  Dispatch must agree exactly; combine sums must agree
+exactly (same order, both double)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from tests import bruteforce as bf
+
+
+def _case(rng, P, T, k, E, H=8, srow=0, with_w=True, dup=True, oob=True):
+    counts = rng.integers(0, T + 1, size=P).astype(np.int32)
+    ids = rng.integers(0, E, size=(P, T, k)).astype(np.int32)
+    if dup and k > 1:
+        m = rng.random((P, T)) < 0.3
+        ids[m, 1] = ids[m, 0]
+    if oob:
+        m = rng.random((P, T, k)) < 0.1
+        ids[m] = rng.choice([-1, -7, E, E + 3], size=int(m.sum()))
+    payload = rng.integers(0, 256, size=(P, T, 2 * H)).astype(np.uint8)
+    scales = rng.integers(0, 256, size=(P, T, srow)).astype(np.uint8) if srow else None
+    weights = rng.standard_normal((P, T, k)).astype(np.float32) if with_w else None
+    return counts, payload, ids, weights, scales
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
+SHAPES = [(1, 5, 3, 4), (2, 3, 2, 4), (3, 4, 1, 3), (4, 6, 3, 8), (4, 8, 4, 16), (3, 7, 2, 12)]
+
+
+@pytest.mark.parametrize("P,T,k,E", SHAPES)
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_dispatch_matches_bruteforce(P, T, k, E, seed):
+    rng = np.random.default_rng(1000 * seed + 17 * P + T)
+    srow = 4 if seed == 1 else 0
+    counts, payload, ids, weights, scales = _case(rng, P, T, k, E, srow=srow, with_w=(seed != 2))
+    got = oracle.dispatch(counts, payload, ids, weights, scales, E=E)
+    recv = bf.dispatch(counts, payload, ids, weights, scales, E)
+    assert np.array_equal(got["ids"], bf.recv_ids_plane(recv, P, T, k, E))
+    cnt, slots = bf.counts_and_slots(recv, P, T)
+    assert np.array_equal(got["counts"], cnt)
+    for r in range(P):
+        n = len(slots[r])
+        assert list(got["slots"][r, :n]) == slots[r]
+        assert np.all(got["slots"][r, n:] == -1)
+        assert set(np.nonzero(got["valid"][r])[0]) == set(recv[r])
+        for q, (pl, sc, idr, w) in recv[r].items():
+            assert bytes(got["payload"][r, q]) == pl
+            if sc is not None:
+                assert bytes(got["scales"][r, q]) == sc
+            if w is not None:
+                assert list(got["weights"][r, q]) == pytest.approx(w, abs=0, rel=0)
+
+
+@pytest.mark.parametrize("P,T,k,E", SHAPES)
+def test_dispatch_custom_invalid_id(P, T, k, E):
+    rng = np.random.default_rng(5 + P)
+    counts, payload, ids, weights, scales = _case(rng, P, T, k, E)
+    got = oracle.dispatch(counts, payload, ids, weights, scales, E=E, invalid_id=-1)
+    recv = bf.dispatch(counts, payload, ids, weights, scales, E)
+    assert np.array_equal(got["ids"], bf.recv_ids_plane(recv, P, T, k, -1))
+
+
+def test_dispatch_destination_subset_matches_full():
+    rng = np.random.default_rng(9)
+    P, T, k, E = 4, 6, 3, 8
+    counts, payload, ids, weights, scales = _case(rng, P, T, k, E)
+    full = oracle.dispatch(counts, payload, ids, weights, scales, E=E)
+    part = oracle.dispatch(counts, payload, ids, weights, scales, E=E, r0=1, r1=3)
+    for key in ("ids", "valid", "counts", "slots", "payload"):
+        assert np.array_equal(full[key][1:3], part[key])
+
+
+@pytest.mark.parametrize("P,T,k,E", SHAPES)
+def test_combine_bf16_matches_bruteforce(P, T, k, E):
+    rng = np.random.default_rng(77 + P * T)
+    H = 8
+    counts, payload, ids, weights, scales = _case(rng, P, T, k, E, H=H)
+    eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
+    ref, y = oracle.combine_bf16(counts, ids, eo, E=E)
+    want = bf.combine_bf16(counts, ids, eo, E)
+    for s in range(P):
+        for t in range(T):
+            if t < counts[s]:
+                assert list(ref[s, t]) == want[(s, t)]
+                assert all(int(y[s, t, h]) == oracle.double_to_bf16(want[(s, t)][h]) for h in range(H))
+            else:
+                assert np.all(ref[s, t] == 0) and np.all(y[s, t] == 0)
+
+
+def test_combine_token_agrees_with_array_form():
+    rng = np.random.default_rng(3)
+    P, T, k, E, H = 4, 5, 3, 8, 16
+    counts, _, ids, _, _ = _case(rng, P, T, k, E, H=H)
+    eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
+    ref, y = oracle.combine_bf16(counts, ids, eo, E=E)
+    for s in range(P):
+        for t in range(int(counts[s])):
+            r1, y1 = oracle.combine_token_bf16(ids[s, t], eo[:, s * T + t], E=E)
+            assert np.array_equal(r1, ref[s, t]) and np.array_equal(y1, y[s, t])
+    ref2, y2 = oracle.combine_bf16(counts, ids, eo, E=E, s0=2, s1=4)
+    assert np.array_equal(ref2, ref[2:4]) and np.array_equal(y2, y[2:4])
