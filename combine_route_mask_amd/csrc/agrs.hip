@@ -1,0 +1,146 @@
+// gfx950 kernels of the all-gatherv / reduce-scatterv exchange (vLLM
+// "device_communicators.all2all", AgRsAll2AllManager: dispatch gathers
+// [hidden, topk_weights, topk_ids] from every rank along dim 0 with
+// per-rank sizes; combine reduce-scatters the hidden rows with the same
+// sizes) between P virtual ranks on one GPU.
+//
+// One workgroup per global row j of the concatenation.  All-gatherv reads
+// the row once and writes it to all P ranks; reduce-scatterv reads row j
+// of every rank's partial, sums in fp32 and writes the owning rank's row.
+#include "formats.h"
+#include "moe_ep_internal.h"
+
+namespace moe_ep {
+namespace {
+
+constexpr int kVpt = 2;
+
+// Rank whose segment [off[q], off[q+1]) holds global row j (empty segments
+// are skipped).  Uniform across the workgroup.
+__device__ __forceinline__ int segment_of(const int32_t *off, int P, int64_t j)
+{
+    int q = 0;
+    while (q + 1 < P && off[q + 1] <= j)
+        ++q;
+    return q;
+}
+
+// Read one row once (two words of type W per thread per pass) and write it
+// to all P ranks: rank r's copy at dst0 + r * stride.
+template <typename W>
+__device__ __forceinline__ void bcast_words(const uint8_t *src, int64_t nbytes, int P, uint8_t *dst0,
+                                            int64_t stride)
+{
+    const int64_t n = nbytes / (int64_t)sizeof(W);
+    const W *s = reinterpret_cast<const W *>(src);
+    for (int64_t i0 = threadIdx.x; i0 < n; i0 += 2 * kBlock) {
+        const int64_t i1 = i0 + kBlock;
+        const bool p1 = i1 < n;
+        const W v0 = s[i0];
+        const W v1 = p1 ? s[i1] : v0;
+        for (int r = 0; r < P; ++r) {
+            W *d = reinterpret_cast<W *>(dst0 + (int64_t)r * stride);
+            d[i0] = v0;
+            if (p1)
+                d[i1] = v1;
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void allgatherv_kernel(AllGatherArgs a, int64_t rows)
+{
+    for (int64_t j = blockIdx.x; j < rows; j += gridDim.x) {
+        const int q = segment_of(a.off, a.P, j);
+        const int64_t i = j - a.off[q];
+        for (int p = 0; p < a.nplanes; ++p) {
+            const AgPlane &pl = a.pl[p];
+            const uint8_t *src = pl.in + (int64_t)q * pl.in_stride + i * pl.row_bytes;
+            uint8_t *dst0 = pl.out + j * pl.row_bytes;
+            const uint64_t align = (uint64_t)(uintptr_t)pl.in | (uint64_t)(uintptr_t)pl.out |
+                                   (uint64_t)pl.in_stride | (uint64_t)pl.out_stride |
+                                   (uint64_t)pl.row_bytes;
+            if ((align & 15) == 0)
+                bcast_words<uint4>(src, pl.row_bytes, a.P, dst0, pl.out_stride);
+            else if ((align & 3) == 0)
+                bcast_words<uint32_t>(src, pl.row_bytes, a.P, dst0, pl.out_stride);
+            else
+                bcast_words<uint8_t>(src, pl.row_bytes, a.P, dst0, pl.out_stride);
+        }
+    }
+}
+
+__global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterArgs a, int64_t rows)
+{
+    const int64_t nvec = a.H >> 3;
+    for (int64_t j = blockIdx.x; j < rows; j += gridDim.x) {
+        const int r = segment_of(a.off, a.P, j);
+        const int64_t i = j - a.off[r];
+        for (int64_t b = 0; b < nvec; b += kBlock * kVpt) {
+            float acc[kVpt][8];
+#pragma unroll
+            for (int u = 0; u < kVpt; ++u)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    acc[u][e] = 0.0f;
+            for (int q = 0; q < a.P; ++q) {
+                const uint4 *src = reinterpret_cast<const uint4 *>(a.in + (int64_t)q * a.in_stride + j * a.H);
+                uint4 v[kVpt];
+#pragma unroll
+                for (int u = 0; u < kVpt; ++u) {
+                    const int64_t k = b + u * kBlock + threadIdx.x;
+                    if (k < nvec)
+                        v[u] = src[k];
+                }
+#pragma unroll
+                for (int u = 0; u < kVpt; ++u) {
+                    const int64_t k = b + u * kBlock + threadIdx.x;
+                    if (k < nvec) {
+                        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            float lo, hi;
+                            unpack_bf16x2(w[e], lo, hi);
+                            acc[u][2 * e] += lo;
+                            acc[u][2 * e + 1] += hi;
+                        }
+                    }
+                }
+            }
+            uint4 *dst = reinterpret_cast<uint4 *>(a.out + (int64_t)r * a.out_stride + i * a.H);
+#pragma unroll
+            for (int u = 0; u < kVpt; ++u) {
+                const int64_t k = b + u * kBlock + threadIdx.x;
+                if (k < nvec) {
+                    uint4 o;
+                    o.x = pack_bf16x2(acc[u][0], acc[u][1]);
+                    o.y = pack_bf16x2(acc[u][2], acc[u][3]);
+                    o.z = pack_bf16x2(acc[u][4], acc[u][5]);
+                    o.w = pack_bf16x2(acc[u][6], acc[u][7]);
+                    dst[k] = o;
+                }
+            }
+        }
+    }
+}
+
+inline unsigned grid_for(int64_t nitems)
+{
+    const int64_t cap = 256 * 8 * 64;
+    return (unsigned)(nitems < 1 ? 1 : (nitems < cap ? nitems : cap));
+}
+
+} // namespace
+
+hipError_t launch_allgatherv(const AllGatherArgs &a, int64_t rows, hipStream_t s)
+{
+    hipLaunchKernelGGL(allgatherv_kernel, dim3(grid_for(rows)), dim3(kBlock), 0, s, a, rows);
+    return hipGetLastError();
+}
+
+hipError_t launch_reduce_scatterv(const ReduceScatterArgs &a, int64_t rows, hipStream_t s)
+{
+    hipLaunchKernelGGL(reduce_scatterv_kernel, dim3(grid_for(rows)), dim3(kBlock), 0, s, a, rows);
+    return hipGetLastError();
+}
+
+} // namespace moe_ep

@@ -1,0 +1,77 @@
+// Kernel argument blocks and launchers shared by the host library and the
+// gfx950 kernels.  Kernel arguments are passed by value (a few hundred
+// bytes), so one launch needs no device-side descriptor.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "moe_ep.h"
+
+namespace moe_ep {
+
+constexpr int kBlock = 256;          // threads per workgroup (4 wave64)
+constexpr int kMaxPlanes = 8;
+
+// Byte offsets of one rank's planes inside its workspace region.
+struct Layout {
+    int64_t region;                  // size_per_rank
+    int64_t payload, scales, ids, weights, slots, counts, src_offsets, masks;
+    int64_t land_codes, land_scales; // FP8 combine landing plane, -1 if absent
+    int64_t row_bytes, srow_bytes;   // payload / scale row bytes
+    int64_t total;                   // bytes needed per region
+};
+
+struct DispatchArgs {
+    const uint8_t *payload;          // [P][T][row_bytes]
+    const uint8_t *scales;           // [P][T][srow_bytes] or null
+    const int32_t *ids;              // [P][T][k]
+    const float *weights;            // [P][T][k] or null
+    uint8_t *ws;                     // region r at ws + r * region
+    int64_t region;
+    int64_t off_payload, off_scales, off_ids, off_weights, off_slots, off_counts,
+        off_src_offsets, off_masks;
+    int64_t row_bytes, srow_bytes;
+    int32_t P, T, k, E, epr, invalid_id;
+    int32_t n[MOE_EP_MAX_RANKS];     // local token counts
+};
+
+struct CombineArgs {
+    const uint16_t *eo;              // [P][P*T][H] bf16
+    uint16_t *out;                   // [P][T][H] bf16
+    uint8_t *ws;
+    int64_t region, off_masks, off_land_codes, off_land_scales;
+    int32_t P, T, H;
+    int32_t n[MOE_EP_MAX_RANKS];
+};
+
+struct AgPlane {
+    const uint8_t *in;
+    int64_t in_stride;
+    uint8_t *out;
+    int64_t out_stride;
+    int64_t row_bytes;
+};
+
+struct AllGatherArgs {
+    AgPlane pl[kMaxPlanes];
+    int32_t nplanes, P;
+    int32_t off[MOE_EP_MAX_RANKS + 1]; // exclusive prefix of sizes
+};
+
+struct ReduceScatterArgs {
+    const uint16_t *in;              // rank q at in + q * in_stride (elements)
+    int64_t in_stride;
+    uint16_t *out;                   // rank r at out + r * out_stride (elements)
+    int64_t out_stride;
+    int32_t P, H;
+    int32_t off[MOE_EP_MAX_RANKS + 1];
+};
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
+hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s);
+hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s);
+hipError_t launch_allgatherv(const AllGatherArgs &a, int64_t rows, hipStream_t s);
+hipError_t launch_reduce_scatterv(const ReduceScatterArgs &a, int64_t rows, hipStream_t s);
+
+} // namespace moe_ep

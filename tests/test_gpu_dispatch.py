@@ -1,0 +1,181 @@
+"""GPU dispatch parity: the HIP path (through the C ABI) against the CPU
+oracle, bit-exact -- receive payload / scale / ids / weights planes of
+every valid slot, invalid-id markers on every other slot, per-source
+counts, source offsets and the ascending valid-slot list.
+
+Sizes: the small cases span several 256-thread tiles and ragged tails;
+the full workloads run at their real shapes (the largest one compares
+every id plane and count in full and the payload planes of sampled
+destination ranks)."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+from tests.gpu_util import DispatchCase, gpu_inputs, log, random_byte_case
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    from combine_route_mask_amd import moe_ep
+    assert torch.cuda.is_available() and moe_ep.moe_ep_is_supported()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _exchange(w, T_cap=None, **kw):
+    from combine_route_mask_amd.moe_ep import MoeEpExchange
+    return MoeEpExchange(w.P, w.E, w.k, T_cap or w.T, w.H, dispatch_format=w.fmt,
+                         combine_format=w.combine, **kw)
+
+
+def _check(c: DispatchCase, out, dests=None, invalid_id=None, with_weights=True):
+    w = c.w
+    P, T, k = w.P, w.T, w.k
+    inv = w.E if invalid_id is None else invalid_id
+    full = oracle.dispatch(c.counts, c.payload, c.ids, c.weights if with_weights else None,
+                           c.scales, E=w.E, invalid_id=inv, want_payload=False)
+    torch.cuda.synchronize()
+    ids = out["ids"].cpu().numpy()
+    assert np.array_equal(ids, full["ids"]), "ids plane / markers differ"
+    assert np.array_equal(out["counts"].cpu().numpy(), full["counts"]), "counts differ"
+    offs = out["src_offsets"].cpu().numpy()
+    cnt = full["counts"]
+    assert np.array_equal(offs[:, :P], np.cumsum(cnt, axis=1) - cnt), "source offsets differ"
+    assert np.array_equal(offs[:, P], cnt.sum(1)), "totals differ"
+    slots = out["slots"].cpu().numpy()
+    for r in range(P):
+        n = int(cnt[r].sum())
+        assert np.array_equal(slots[r, :n], full["slots"][r, :n]), f"slot list of rank {r} differs"
+    for r in (range(P) if dests is None else dests):
+        one = oracle.dispatch(c.counts, c.payload, c.ids, c.weights if with_weights else None,
+                              c.scales, E=w.E, invalid_id=inv, r0=r, r1=r + 1)
+        v = one["valid"][0].astype(bool)
+        pl = out["payload"][r].cpu().numpy()
+        assert np.array_equal(pl[v], one["payload"][0][v]), f"payload of rank {r} differs"
+        if c.scales is not None:
+            sc = out["scales"][r].cpu().numpy()
+            assert np.array_equal(sc[v], one["scales"][0][v]), f"scales of rank {r} differ"
+        if with_weights:
+            wt = out["weights"][r].cpu().numpy()
+            assert np.array_equal(wt[v].view(np.uint32), one["weights"][0][v].view(np.uint32)), \
+                f"weights of rank {r} differ"
+
+
+def _run(c: DispatchCase, ex=None, T_cap=None, dests=None, invalid_id=None, with_weights=True):
+    w = c.w
+    log(f"dispatch case: {w.name} P={w.P} T={w.T} H={w.H} k={w.k} E={w.E} fmt={w.fmt} "
+        f"counts[:8]={c.counts[:8].tolist()}")
+    ex = ex or _exchange(w, T_cap, has_weights=with_weights, invalid_expert_id=invalid_id)
+    pl, sc, ids, wt = gpu_inputs(c)
+    out = ex.dispatch(pl, ids, wt if with_weights else None, scales=sc,
+                      num_tokens=c.counts.tolist(), runtime_max_tokens_per_rank=w.T)
+    _check(c, out, dests, invalid_id, with_weights)
+    return ex
+
+
+SMALL = [
+    W.TINY,
+    dataclasses.replace(W.TINY, name="p1", P=1, E=4, T=300, n_lo=0, n_hi=300, H=64),
+    dataclasses.replace(W.TINY, name="k1", k=1, T=70, n_lo=1, n_hi=70),
+    dataclasses.replace(W.TINY, name="ragged P5 T37 H136", P=5, E=20, k=3, T=37, H=136,
+                        n_lo=0, n_hi=37),
+    dataclasses.replace(W.TINY, name="P64 E64 epr1", P=64, E=64, k=8, T=9, H=64, n_lo=0, n_hi=9),
+    dataclasses.replace(W.TINY, name="two-pass rows H8200", P=3, E=12, k=4, T=5, H=8200,
+                        n_lo=1, n_hi=5),
+    dataclasses.replace(W.EP8_MXFP8, name="mxfp8 small", T=33, H=96, n_lo=0, n_hi=33),
+    dataclasses.replace(W.EP64_NVFP4, name="nvfp4 small", P=16, E=64, T=20, H=64, n_lo=3, n_hi=20),
+    dataclasses.replace(W.TINY, name="many slots P16 T1500", P=16, E=64, k=4, T=1500, H=32,
+                        n_lo=700, n_hi=1500),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+@pytest.mark.parametrize("seed", [11, 12])
+def test_dispatch_small(w, seed):
+    c = random_byte_case(w, seed, oob=(seed == 12), dup=(seed == 12))
+    _run(c)
+
+
+def test_dispatch_without_weights_and_custom_marker():
+    w = dataclasses.replace(W.TINY, name="noweights", T=40, n_lo=0, n_hi=40)
+    c = random_byte_case(w, 5, oob=True)
+    _run(c, invalid_id=-1, with_weights=False)
+
+
+def test_dispatch_empty_ranks_and_T1():
+    w = dataclasses.replace(W.TINY, name="empty", T=24, H=128)
+    c = random_byte_case(w, 6, counts=[0, 24, 0, 3])
+    _run(c)
+    w1 = dataclasses.replace(W.TINY, name="T1", T=1, H=128)
+    _run(random_byte_case(w1, 7, counts=[1, 0, 1, 1]))
+
+
+def test_dispatch_stale_slots_are_remarked():
+    """Two steps on one handle: the second has a smaller T, other counts
+    and other routing; every slot of step 2 must reflect step 2 only."""
+    w = dataclasses.replace(W.TINY, name="stale", T=64, H=256, n_lo=30, n_hi=64)
+    ex = _run(random_byte_case(w, 21), T_cap=64)
+    w2 = dataclasses.replace(w, T=48)
+    _run(random_byte_case(w2, 22, counts=[48, 5, 0, 17]), ex=ex)
+    # and a third step back at full size, mostly empty
+    _run(random_byte_case(w, 23, counts=[1, 0, 2, 0]), ex=ex)
+
+
+def test_dispatch_runtime_T_below_capacity():
+    w = dataclasses.replace(W.EP8_BF16, name="T below cap", T=100, n_lo=10, n_hi=100, H=512)
+    _run(random_byte_case(w, 31), T_cap=128)
+
+
+def test_dispatch_full_ep8_bf16():
+    _run(random_byte_case(W.EP8_BF16, W.EP8_BF16.seed))
+
+
+def test_dispatch_full_ep8_mxfp8_zipf():
+    _run(random_byte_case(W.EP8_MXFP8, W.EP8_MXFP8.seed))
+
+
+@pytest.mark.parametrize("w", [W.EP64_BF16, W.EP64_NVFP4], ids=lambda w: w.name)
+def test_dispatch_full_ep64(w):
+    c = random_byte_case(w, w.seed)
+    ex = _run(c, dests=[0, 37, 63])
+    ex.destroy()
+    del ex
+    torch.cuda.empty_cache()
+
+
+def test_dispatch_is_deterministic():
+    w = dataclasses.replace(W.EP8_BF16, name="determinism", H=1024)
+    c = random_byte_case(w, 41)
+    ex = _exchange(w)
+    pl, sc, ids, wt = gpu_inputs(c)
+    a = ex.dispatch(pl, ids, wt, num_tokens=c.counts.tolist())
+    snap = {k: v.clone() for k, v in a.items() if isinstance(v, torch.Tensor)}
+    b = ex.dispatch(pl, ids, wt, num_tokens=c.counts.tolist())
+    for k, v in snap.items():
+        assert torch.equal(v, b[k]), k
+
+
+def test_dispatch_rejects_bad_steps():
+    from combine_route_mask_amd import moe_ep
+    w = dataclasses.replace(W.TINY, name="errors")
+    c = random_byte_case(w, 51)
+    ex = _exchange(w)
+    pl, sc, ids, wt = gpu_inputs(c)
+    with pytest.raises(moe_ep.MoeEpError) as e:
+        moe_ep.moe_ep_dispatch(ex.handle, pl, None, ids, wt, c.counts.tolist(), w.T + 1)
+    assert e.value.code == moe_ep.ERR_CAPACITY
+    with pytest.raises(moe_ep.MoeEpArgError):
+        moe_ep.moe_ep_dispatch(ex.handle, pl, None, ids, wt, [w.T + 1] + [0] * (w.P - 1), w.T)
+    with pytest.raises(moe_ep.MoeEpArgError):
+        moe_ep.moe_ep_dispatch(ex.handle, pl, None, ids, None, c.counts.tolist(), w.T)
+    with pytest.raises(moe_ep.MoeEpArgError):
+        moe_ep.moe_ep_dispatch(ex.handle, pl, pl, ids, wt, c.counts.tolist(), w.T)
+    with pytest.raises(moe_ep.MoeEpError) as e:
+        moe_ep.moe_ep_combine(ex.handle, pl, pl)
+    assert e.value.code == moe_ep.ERR_BAD_STATE
