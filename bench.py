@@ -2,7 +2,9 @@
 
 One step = one dispatch + one combine over all P virtual EP ranks of the
 workload, inputs (token rows, ids, weights, expert outputs) resident in
-HBM.  Prints one JSON line:
+HBM.  Ten consecutive steps (two launches each) are captured in a HIP
+graph that is replayed until the requested number of steps has run (the
+eager two-launch time is reported beside it).  Prints one JSON line:
 
   value        tokens/s = N / step time (N = sum of local token counts)
   roofline     the dominant kernel's algorithmic bytes per launch / its
@@ -69,8 +71,14 @@ def step_bytes(w, N, M):
 
 
 class Setup:
+    """Inputs of one workload resident on the GPU, a handle, and the two
+    launches of a step through the raw C ABI (pointers precomputed, so the
+    host adds only a ctypes call per launch)."""
+
     def __init__(self, w, seed=None):
+        import ctypes as C
         import torch
+        from combine_route_mask_amd import moe_ep
         from combine_route_mask_amd.moe_ep import MoeEpExchange
         self.w = w
         dev = torch.device("cuda")
@@ -88,58 +96,144 @@ class Setup:
         self.counts = self.R.counts.tolist()
         self.N = int(self.R.counts.sum())
         self.M = pair_count(w, self.R)
+        # first step through the checked binding (sets up the views)
+        self.views = self.ex.dispatch(self.payload, self.ids, self.weights, scales=self.scales,
+                                      num_tokens=self.counts, runtime_max_tokens_per_rank=w.T)
+        self.ex.combine(self.eo, self.out)
+        self._lib = moe_ep.lib
+        self._h = self.ex.handle
+        self._args = (C.c_void_p(self.payload.data_ptr()),
+                      C.c_void_p(self.scales.data_ptr()) if self.scales is not None else None,
+                      C.c_void_p(self.ids.data_ptr()), C.c_void_p(self.weights.data_ptr()),
+                      (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T))
+        self._eo = C.c_void_p(self.eo.data_ptr())
+        self._out = C.c_void_p(self.out.data_ptr())
 
     def dispatch(self):
-        self.ex.dispatch(self.payload, self.ids, self.weights, scales=self.scales,
-                         num_tokens=self.counts, runtime_max_tokens_per_rank=self.w.T)
+        import torch
+        st = torch.cuda.current_stream().cuda_stream
+        rc = self._lib.moe_ep_dispatch(self._h, *self._args, st, None)
+        if rc:
+            raise RuntimeError(self._lib.moe_ep_last_error().decode())
 
     def combine(self):
-        self.ex.combine(self.eo, self.out)
+        import torch
+        st = torch.cuda.current_stream().cuda_stream
+        rc = self._lib.moe_ep_combine(self._h, self._eo, self._out, st)
+        if rc:
+            raise RuntimeError(self._lib.moe_ep_last_error().decode())
 
     def free(self):
         self.ex.destroy()
-        del self.eo, self.payload, self.ex
+        del self.eo, self.payload, self.ex, self.views
+
+
+def _graph(fn, reps=1):
+    import torch
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        fn()  # warm the stream once outside capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for _ in range(reps):
+                fn()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    return g
+
+
+def _time(fn, iters):
+    import torch
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(iters):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b)
 
 
 def measure(setup, steps, warmup, flush_bytes=0):
-    """Time `steps` dispatch+combine steps after `warmup` untimed ones.
-    Events on the current stream (the one the kernels are launched on)
-    bracket the whole timed region and every single launch."""
+    """Step time of `steps` dispatch+combine steps after `warmup` untimed
+    ones, eager (two C-ABI launches per step) and as one HIP-graph replay
+    per step; per-launch kernel times from graphs of 20 back-to-back
+    launches of one kernel.  All events sit on the launch stream."""
     import torch
-    stream = torch.cuda.current_stream()
-    flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda") if flush_bytes else None
+
+    def step():
+        setup.dispatch()
+        setup.combine()
+
     for _ in range(warmup):
-        setup.dispatch()
-        setup.combine()
+        step()
     torch.cuda.synchronize()
-    # the recv counts of the step must match the host-side pair count
-    got_M = int(setup.ex.dispatch(setup.payload, setup.ids, setup.weights, scales=setup.scales,
-                                  num_tokens=setup.counts,
-                                  runtime_max_tokens_per_rank=setup.w.T)["counts"].sum().item())
+    # the step's receive counts must match the host-side pair count
+    got_M = int(setup.views["counts"].sum().item())
     assert got_M == setup.M, (got_M, setup.M)
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        if flush is not None:
-            flush.fill_(i & 0xFF)  # untimed: evicts the 256 MB last-level cache
-        ev[i][0].record(stream)
-        setup.dispatch()
-        ev[i][1].record(stream)
-        setup.combine()
-        ev[i][2].record(stream)
-    stop.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    t_disp = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)])
-    t_comb = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)])
-    total_ms = start.elapsed_time(stop)
-    step_ms = float((t_disp + t_comb).mean()) if flush is not None else total_ms / steps
-    return {"ms_per_step": step_ms, "dispatch_ms": float(t_disp.mean()),
-            "combine_ms": float(t_comb.mean()), "dispatch_ms_median": float(np.median(t_disp)),
-            "combine_ms_median": float(np.median(t_comb)), "wall_s": wall}
+    ref_out = setup.out.clone()
+    ref_ids = setup.views["ids"].clone()
+
+    eager_ms = _time(step, steps) / steps
+    # one graph holds `per` consecutive steps, so a small step is not bound
+    # by the host's graph-launch rate; `steps` is rounded up to a multiple
+    per = 1 if flush_bytes else 10
+    replays = -(-steps // per)
+    g_step = _graph(step, per)
+    for _ in range(max(1, warmup // per)):
+        g_step.replay()
+    wall0 = time.perf_counter()
+    if flush_bytes:
+        # cold: a 1 GiB fill between steps (untimed) evicts the last-level cache
+        flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for i in range(steps):
+            flush.fill_(i & 0xFF)
+            ev[i][0].record(stream)
+            g_step.replay()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        graph_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        del flush
+    else:
+        graph_ms = _time(g_step.replay, replays) / (replays * per)
+    wall = time.perf_counter() - wall0
+    # graph replays must reproduce the eager step bit for bit
+    assert torch.equal(setup.out.view(torch.int16), ref_out.view(torch.int16))
+    assert torch.equal(setup.views["ids"], ref_ids)
+
+    reps = 20
+    g_d = _graph(setup.dispatch, reps)
+    g_c = _graph(setup.combine, reps)
+    g_d.replay()
+    g_c.replay()
+    it = max(2, steps // reps)
+    disp_ms = _time(g_d.replay, it) / (it * reps)
+    comb_ms = _time(g_c.replay, it) / (it * reps)
+    del g_step, g_d, g_c
+    return {"ms_per_step": graph_ms, "eager_ms_per_step": eager_ms, "dispatch_ms": disp_ms,
+            "combine_ms": comb_ms, "wall_s": wall}
+
+
+def calibrate(nbytes=2 << 30, iters=10):
+    """Achievable HBM bandwidth on this GPU: a plain device copy (read +
+    write, torch copy_) and a fill (write only) of nbytes."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    src.fill_(1)
+    dst.copy_(src)
+    ms_copy = _time(lambda: dst.copy_(src), iters) / iters
+    ms_fill = _time(lambda: dst.fill_(3), iters) / iters
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GBps": 2 * nbytes / (ms_copy / 1e3) / 1e9,
+            "fill_GBps": nbytes / (ms_fill / 1e3) / 1e9, "bytes": nbytes}
 
 
 def summarize(setup, m):
@@ -153,6 +247,7 @@ def summarize(setup, m):
         "ms_per_step": m["ms_per_step"],
         "step_bytes": b["dispatch"] + b["combine"],
         "step_GBps": (b["dispatch"] + b["combine"]) / step_s / 1e9,
+        "eager_ms_per_step": m["eager_ms_per_step"],
         "dispatch_ms": m["dispatch_ms"], "combine_ms": m["combine_ms"],
         "dispatch_GBps": gbs(b["dispatch"], m["dispatch_ms"]),
         "combine_GBps": gbs(b["combine"], m["combine_ms"]),
@@ -211,6 +306,8 @@ def main():
         print(json.dumps({"error": "no gfx950 GPU visible"}))
         sys.exit(1)
     w = WORKLOADS[args.config]
+    print("[bench] calibrating copy / fill bandwidth", file=sys.stderr, flush=True)
+    calib = calibrate()
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     setup = Setup(w)
     m = measure(setup, args.steps, args.warmup, flush_bytes=(1 << 30) if args.cold else 0)
@@ -229,7 +326,8 @@ def main():
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
-                "bytes_per_launch": dom_bytes, "launch_ms": dom_ms}
+                "bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
+                "frac_of_measured_copy": achieved / calib["copy_GBps"]}
 
     also = []
     for name in [a for a in args.also.split(",") if a]:
@@ -238,7 +336,8 @@ def main():
         wa = WORKLOADS[name]
         print(f"[bench] setting up {wa.name}", file=sys.stderr, flush=True)
         sa = Setup(wa)
-        ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2))
+        ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2),
+                     flush_bytes=(1 << 30) if args.cold else 0)
         ra, _ = summarize(sa, ma)
         sa.free()
         del sa
@@ -265,6 +364,7 @@ def main():
         "detail": res,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "calibration": calib,
         "also": also,
     }
     print(json.dumps(line))

@@ -158,7 +158,8 @@ def test_dispatch_is_deterministic():
     snap = {k: v.clone() for k, v in a.items() if isinstance(v, torch.Tensor)}
     b = ex.dispatch(pl, ids, wt, num_tokens=c.counts.tolist())
     for k, v in snap.items():
-        assert torch.equal(v, b[k]), k
+        # bit patterns: never-written slots may hold NaN bytes from earlier use
+        assert torch.equal(v.view(torch.uint8), b[k].view(torch.uint8)), k
 
 
 def test_dispatch_rejects_bad_steps():
