@@ -13,22 +13,81 @@
 // contraction, so no matrix cores are used.  Rows move as 16-byte vectors
 // (global_load/store_dwordx4); a workgroup reads a token row once and
 // writes it to every destination in its mask.
+#include <algorithm>
+
 #include "formats.h"
 #include "moe_ep_internal.h"
+
+// Tuning knobs (compile-time; defaults are the measured best on MI355X).
+#ifndef MOE_EP_NT_STORE
+#define MOE_EP_NT_STORE 1     // dispatch row stores bypass the caches' retention
+#endif
+#ifndef MOE_EP_DISPATCH_VPT
+#define MOE_EP_DISPATCH_VPT 4 // 16-byte vectors per thread in a dispatch row chunk
+#endif
+#ifndef MOE_EP_DISPATCH_NT_LOAD
+#define MOE_EP_DISPATCH_NT_LOAD 0 // dispatch reads each token row once
+#endif
+#ifndef MOE_EP_SCATTER_GRID
+#define MOE_EP_SCATTER_GRID 131072 // most payload-scatter workgroups of a dispatch launch
+#endif
+// BF16 combine shapes: (16-byte vectors per thread, ranks loaded at once,
+// non-temporal output stores) for outputs that fit the 256 MB last-level
+// cache and for larger ones.
+#ifndef MOE_EP_COMBINE_SMALL
+#define MOE_EP_COMBINE_SMALL 1, 8, 0
+#endif
+#ifndef MOE_EP_COMBINE_LARGE
+#define MOE_EP_COMBINE_LARGE 4, 2, 1
+#endif
+#ifndef MOE_EP_COMBINE_LARGE_BYTES
+#define MOE_EP_COMBINE_LARGE_BYTES (128ll << 20)
+#endif
 
 namespace moe_ep {
 namespace {
 
-constexpr int kVpt = 4;        // 16-byte vectors per thread per pass (combine)
-constexpr int kScanUnroll = 4; // 256-slot chunks per scan step
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kScanUnroll = 4;          // 256-slot chunks per scan step
 constexpr int kWaves = kBlock / 64;
+constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
+constexpr int kDVpt = MOE_EP_DISPATCH_VPT;
+constexpr int kDChunk = kBlock * kDVpt; // 16-byte vectors per dispatch row chunk
+
+__device__ __forceinline__ u32x4 load16_nt(const void *p)
+{
+    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+}
+
+__device__ __forceinline__ void store16(void *p, u32x4 v)
+{
+#if MOE_EP_NT_STORE
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
+#else
+    *reinterpret_cast<u32x4 *>(p) = v;
+#endif
+}
 
 // Destination-rank mask of one token: bit r set when one of its k ids is an
 // expert of rank r (experts e / epr == r).  OR-ing the bits deduplicates
 // tokens with several experts on one rank; ids outside [0, E) set nothing.
-__device__ __forceinline__ uint64_t route_mask(const int32_t *idrow, int k, int E, int epr)
+// For k <= 16 all k loads are issued before the first is used.
+__device__ __forceinline__ uint64_t route_mask(const int32_t *__restrict__ idrow, int k, int E,
+                                               int epr)
 {
     uint64_t m = 0;
+    if (k <= 16) {
+        int32_t id[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            id[j] = j < k ? idrow[j] : -1;
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+            if (id[j] >= 0 && id[j] < E)
+                m |= 1ull << (unsigned)(id[j] / epr);
+        return m;
+    }
     for (int j = 0; j < k; ++j) {
         const int id = idrow[j];
         if (id >= 0 && id < E)
@@ -44,40 +103,8 @@ __device__ __forceinline__ int lanes_below(uint64_t bits)
                                           __builtin_amdgcn_mbcnt_lo((uint32_t)bits, 0u));
 }
 
-// Copy one row of nbytes (multiple of 16, 16-byte aligned) to every rank in
-// mask: rank r's copy at dst0 + r * stride.  The row is read once into
-// registers, four 16-byte vectors per thread per pass (kBlock * 64 bytes),
-// then stored once per destination rank.
-__device__ __forceinline__ void copy_row_x16(const uint8_t *src, int64_t nbytes, uint64_t mask,
-                                             uint8_t *dst0, int64_t stride)
-{
-    const int64_t nvec = nbytes >> 4;
-    const uint4 *s4 = reinterpret_cast<const uint4 *>(src);
-    for (int64_t b = threadIdx.x; b < nvec; b += 4 * kBlock) {
-        const int64_t i0 = b, i1 = b + kBlock, i2 = b + 2 * kBlock, i3 = b + 3 * kBlock;
-        const bool p1 = i1 < nvec, p2 = i2 < nvec, p3 = i3 < nvec;
-        const uint4 zero = {0u, 0u, 0u, 0u};
-        const uint4 v0 = s4[i0];
-        const uint4 v1 = p1 ? s4[i1] : zero;
-        const uint4 v2 = p2 ? s4[i2] : zero;
-        const uint4 v3 = p3 ? s4[i3] : zero;
-        uint64_t m = mask;
-        while (m) {
-            const int r = __builtin_ctzll(m);
-            m &= m - 1;
-            uint4 *d4 = reinterpret_cast<uint4 *>(dst0 + (int64_t)r * stride);
-            d4[i0] = v0;
-            if (p1)
-                d4[i1] = v1;
-            if (p2)
-                d4[i2] = v2;
-            if (p3)
-                d4[i3] = v3;
-        }
-    }
-}
-
-// Same for short rows of any size, word by word (W = uint32_t or uint8_t).
+// Copy one short row (a scale row) to every rank in mask, rank r's copy at
+// dst0 + r * stride, one word W (16, 4 or 1 bytes) per thread access.
 template <typename W>
 __device__ __forceinline__ void copy_row_words(const uint8_t *src, int64_t nbytes, uint64_t mask,
                                                uint8_t *dst0, int64_t stride)
@@ -94,13 +121,14 @@ __device__ __forceinline__ void copy_row_words(const uint8_t *src, int64_t nbyte
     }
 }
 
+// copy_row_words with the widest word the row's size and alignment allow.
 __device__ __forceinline__ void copy_row_any(const uint8_t *src, int64_t nbytes, uint64_t mask,
                                              uint8_t *dst0, int64_t stride)
 {
     const uint64_t align = (uint64_t)(uintptr_t)src | (uint64_t)(uintptr_t)dst0 |
                            (uint64_t)stride | (uint64_t)nbytes;
     if ((align & 15) == 0)
-        copy_row_x16(src, nbytes, mask, dst0, stride);
+        copy_row_words<uint4>(src, nbytes, mask, dst0, stride);
     else if ((align & 3) == 0)
         copy_row_words<uint32_t>(src, nbytes, mask, dst0, stride);
     else
@@ -179,115 +207,210 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
     }
 }
 
-// One source slot q = s*T + t: compute the token's destination mask, store
-// it for combine, write ids/weights (or invalid-id markers) to all P
-// destinations, then read the payload and scale rows once and write them
-// to every destination in the mask.
-__device__ void scatter_token(const DispatchArgs &a, int64_t q)
+// Id and weight planes of destination r for slots [c*kPlaneSlots, ...), in
+// two phases.  First each thread computes one slot's destination mask into
+// LDS (the items of destination 0 also store every token's mask in its
+// source rank's region, for combine).  Then the block walks the chunk's
+// k-word id rows word by word, four words per thread in flight, so
+// consecutive lanes write consecutive words: a slot whose token goes to r
+// gets the token's ids and weights, every other slot k copies of invalid_id.
+__device__ void write_id_planes(const DispatchArgs &a, int r, int64_t c)
+{
+    __shared__ uint64_t smask[kPlaneSlots];
+    const int64_t S = (int64_t)a.P * a.T;
+    const int64_t q0 = c * kPlaneSlots;
+    const int nslot = (int)min<int64_t>(kPlaneSlots, S - q0);
+    if ((int)threadIdx.x < nslot) {
+        const int64_t q = q0 + threadIdx.x;
+        const int s = (int)(q / a.T);
+        const int t = (int)(q - (int64_t)s * a.T);
+        const uint64_t mask = t < a.n[s] ? route_mask(a.ids + q * a.k, a.k, a.E, a.epr) : 0ull;
+        smask[threadIdx.x] = mask;
+        if (r == 0)
+            *reinterpret_cast<uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks +
+                                          (int64_t)t * 8) = mask;
+    }
+    __syncthreads();
+    uint8_t *reg = a.ws + (int64_t)r * a.region;
+    int32_t *__restrict__ ids_out = reinterpret_cast<int32_t *>(reg + a.off_ids) + q0 * a.k;
+    float *__restrict__ w_out = reinterpret_cast<float *>(reg + a.off_weights) + q0 * a.k;
+    const int32_t *__restrict__ ids_in = a.ids + q0 * a.k;
+    const float *__restrict__ w_in = a.weights ? a.weights + q0 * a.k : nullptr;
+    const int nwords = nslot * a.k;
+    constexpr int U = 4;
+    for (int e0 = threadIdx.x; e0 < nwords; e0 += U * kBlock) {
+        int32_t idv[U];
+        float wv[U];
+        bool go[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kBlock;
+            go[u] = e < nwords && ((smask[e / a.k] >> r) & 1u);
+            idv[u] = go[u] ? ids_in[e] : a.invalid_id;
+            wv[u] = (go[u] && w_in) ? w_in[e] : 0.0f;
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            const int e = e0 + u * kBlock;
+            if (e < nwords) {
+                ids_out[e] = idv[u];
+                if (go[u] && w_in)
+                    w_out[e] = wv[u];
+            }
+        }
+    }
+    __syncthreads(); // smask is reused by the block's next item
+}
+
+// Chunk c of token q's payload row (kDVpt 16-byte vectors per thread, lane
+// strided), read once and stored to every destination in the token's mask;
+// chunk 0 also carries the scale row.
+__device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
     const int t = (int)(q - (int64_t)s * a.T);
-    const bool live = t < a.n[s];
-    const int32_t *idrow = a.ids + q * a.k;
-    const uint64_t mask = live ? route_mask(idrow, a.k, a.E, a.epr) : 0ull;
-    if (threadIdx.x == 0)
-        *reinterpret_cast<uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks + (int64_t)t * 8) =
-            mask;
-    for (int i = threadIdx.x; i < a.P * a.k; i += kBlock) {
-        const int r = i / a.k, j = i - r * a.k;
-        uint8_t *reg = a.ws + (int64_t)r * a.region;
-        int32_t id = a.invalid_id;
-        if ((mask >> r) & 1u) {
-            id = idrow[j];
-            if (a.weights)
-                reinterpret_cast<float *>(reg + a.off_weights)[q * a.k + j] = a.weights[q * a.k + j];
-        }
-        reinterpret_cast<int32_t *>(reg + a.off_ids)[q * a.k + j] = id;
-    }
+    if (t >= a.n[s])
+        return;
+    const uint64_t mask = route_mask(a.ids + q * a.k, a.k, a.E, a.epr);
     if (!mask)
         return;
-    copy_row_x16(a.payload + q * a.row_bytes, a.row_bytes, mask,
-                 a.ws + a.off_payload + q * a.row_bytes, a.region);
-    if (a.srow_bytes)
+    const int64_t nvec = a.row_bytes >> 4;
+    const int64_t i0 = c * kDChunk + threadIdx.x;
+    const uint8_t *src = a.payload + q * a.row_bytes;
+    uint8_t *dst0 = a.ws + a.off_payload + q * a.row_bytes;
+    u32x4 v[kDVpt];
+#pragma unroll
+    for (int u = 0; u < kDVpt; ++u)
+        if (i0 + u * kBlock < nvec)
+#if MOE_EP_DISPATCH_NT_LOAD
+            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16));
+#else
+            v[u] = *reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16);
+#endif
+    uint64_t m = mask;
+    while (m) {
+        const int r = __builtin_ctzll(m);
+        m &= m - 1;
+        uint8_t *d = dst0 + (int64_t)r * a.region;
+#pragma unroll
+        for (int u = 0; u < kDVpt; ++u)
+            if (i0 + u * kBlock < nvec)
+                store16(d + (i0 + u * kBlock) * 16, v[u]);
+    }
+    if (c == 0 && a.srow_bytes)
         copy_row_any(a.scales + q * a.srow_bytes, a.srow_bytes, mask,
                      a.ws + a.off_scales + q * a.srow_bytes, a.region);
 }
 
-// Blocks [0, P) do the receive bookkeeping of one destination each; the
-// rest walk the source slots.  The two roles touch disjoint memory.
-__global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a)
+// One launch, three block roles touching disjoint memory:
+//   [0, P)                    receive bookkeeping of destination r
+//   [P, P + plane_blocks)     id / weight planes, (r, slot chunk) items
+//   [P + plane_blocks, grid)  payload scatter, (token, row chunk) items
+// The last two roles loop over their items when there are more items than
+// blocks.
+__global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
+                                                          int64_t plane_blocks, int64_t nchunk)
 {
-    if ((int)blockIdx.x < a.P) {
-        scan_destination(a, (int)blockIdx.x);
+    const int64_t b = blockIdx.x;
+    if (b < a.P) {
+        scan_destination(a, (int)b);
+        return;
+    }
+    if (b < a.P + plane_blocks) {
+        for (int64_t w = b - a.P; w < (int64_t)a.P * nplane; w += plane_blocks)
+            write_id_planes(a, (int)(w / nplane), w % nplane);
         return;
     }
     const int64_t S = (int64_t)a.P * a.T;
-    const int64_t stride = (int64_t)gridDim.x - a.P;
-    for (int64_t q = (int64_t)blockIdx.x - a.P; q < S; q += stride)
-        scatter_token(a, q);
+    const int64_t first = a.P + plane_blocks;
+    const int64_t stride = (int64_t)gridDim.x - first;
+    for (int64_t w = b - first; w < S * nchunk; w += stride)
+        scatter_chunk(a, w / nchunk, w % nchunk);
 }
 
-// BF16 combine: source token (s, t) sums, in fp32 and ascending rank order,
-// row q = s*T + t of every rank in its mask, then rounds to bf16.
-__global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a)
+__device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        float lo, hi;
+        unpack_bf16x2(v[e], lo, hi);
+        acc[2 * e] += lo;
+        acc[2 * e + 1] += hi;
+    }
+}
+
+// BF16 combine: item (token q = s*T + t, row chunk c); each thread owns
+// VPT 16-byte vectors (8 bf16 each) of the output row and sums, in fp32 and
+// ascending rank order, those vectors of row q of every rank in the token's
+// mask.  Expert-output rows are read once (non-temporal loads); the loads
+// of up to G ranks are issued before any is consumed.
+template <int VPT, int G, bool NT_OUT>
+__global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
-    const int64_t rank_stride = S * a.H; // elements
-    const int64_t nvec = a.H >> 3;       // 8 bf16 per 16 bytes
-    for (int64_t q = blockIdx.x; q < S; q += gridDim.x) {
+    const int64_t rank_bytes = S * a.H * 2;
+    const int64_t nvec = a.H >> 3;
+    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
+        const int64_t q = w / nchunk, c = w % nchunk;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
-        if (t >= a.n[s])
+        const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
+        if (t >= a.n[s] || i0 >= nvec)
             continue;
         const uint64_t mask = *reinterpret_cast<const uint64_t *>(
             a.ws + (int64_t)s * a.region + a.off_masks + (int64_t)t * 8);
-        for (int64_t b = 0; b < nvec; b += kBlock * kVpt) {
-            float acc[kVpt][8];
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2 + i0 * 16;
+        bool in[VPT];
 #pragma unroll
-            for (int u = 0; u < kVpt; ++u)
+        for (int u = 0; u < VPT; ++u)
+            in[u] = i0 + u * kBlock < nvec;
+        float acc[VPT][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[u][e] = 0.0f;
-            uint64_t m = mask;
-            while (m) {
-                const int r = __builtin_ctzll(m);
-                m &= m - 1;
-                const uint4 *src = reinterpret_cast<const uint4 *>(a.eo + r * rank_stride + q * a.H);
-                uint4 v[kVpt];
+        for (int u = 0; u < VPT; ++u)
 #pragma unroll
-                for (int u = 0; u < kVpt; ++u) {
-                    const int64_t i = b + u * kBlock + threadIdx.x;
-                    if (i < nvec)
-                        v[u] = src[i];
-                }
+            for (int e = 0; e < 8; ++e)
+                acc[u][e] = 0.0f;
+        uint64_t m = mask;
+        while (m) {
+            int r[G];
+            int cnt = 0;
 #pragma unroll
-                for (int u = 0; u < kVpt; ++u) {
-                    const int64_t i = b + u * kBlock + threadIdx.x;
-                    if (i < nvec) {
-                        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
-#pragma unroll
-                        for (int e = 0; e < 4; ++e) {
-                            float lo, hi;
-                            unpack_bf16x2(w[e], lo, hi);
-                            acc[u][2 * e] += lo;
-                            acc[u][2 * e + 1] += hi;
-                        }
-                    }
+            for (int g = 0; g < G; ++g) {
+                r[g] = 0;
+                if (m) {
+                    r[g] = __builtin_ctzll(m);
+                    m &= m - 1;
+                    cnt = g + 1;
                 }
             }
-            uint4 *dst = reinterpret_cast<uint4 *>(a.out + q * a.H);
+            u32x4 v[G][VPT];
 #pragma unroll
-            for (int u = 0; u < kVpt; ++u) {
-                const int64_t i = b + u * kBlock + threadIdx.x;
-                if (i < nvec) {
-                    uint4 o;
-                    o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-                    o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-                    o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-                    o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-                    dst[i] = o;
-                }
-            }
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+                    if (g < cnt && in[u])
+                        v[g][u] = load16_nt(src + (int64_t)r[g] * rank_bytes + u * kBlock * 16);
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+                    if (g < cnt && in[u])
+                        add_bf16x8(acc[u], v[g][u]);
+        }
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) {
+            if (!in[u])
+                continue;
+            u32x4 o;
+            o[0] = pack_bf16x2(acc[u][0], acc[u][1]);
+            o[1] = pack_bf16x2(acc[u][2], acc[u][3]);
+            o[2] = pack_bf16x2(acc[u][4], acc[u][5]);
+            o[3] = pack_bf16x2(acc[u][6], acc[u][7]);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + (i0 + u * kBlock) * 8);
+            if (NT_OUT)
+                __builtin_nontemporal_store(o, dst);
+            else
+                *dst = o;
         }
     }
 }
@@ -443,32 +566,51 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs 
     }
 }
 
-// Grid of nitems workgroups capped at a whole number of waves of the chip
-// (256 CUs x 8 workgroups); kernels loop over the rest.
-inline unsigned grid_for(int64_t nitems)
+// Grid of nitems workgroups capped at 64 rounds of the chip (256 CUs x 8
+// resident workgroups); kernels loop over the rest.
+inline int64_t grid_for(int64_t nitems)
 {
     const int64_t cap = 256 * 8 * 64;
-    return (unsigned)(nitems < 1 ? 1 : (nitems < cap ? nitems : cap));
+    return nitems < 1 ? 1 : (nitems < cap ? nitems : cap);
 }
+
+inline int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 } // namespace
 
 hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s)
 {
     const int64_t S = (int64_t)a.P * a.T;
-    hipLaunchKernelGGL(dispatch_kernel, dim3(a.P + grid_for(S)), dim3(kBlock), 0, s, a);
+    const int64_t nplane = ceil_div(S, kPlaneSlots);
+    const int64_t plane_blocks = grid_for((int64_t)a.P * nplane);
+    const int64_t nchunk = ceil_div(a.row_bytes >> 4, kDChunk);
+    const int64_t grid = a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
+    hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, a, nplane,
+                       plane_blocks, nchunk);
+    return hipGetLastError();
+}
+
+template <int VPT, int G, bool NT_OUT>
+static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
+{
+    const int64_t nchunk = ceil_div((int64_t)a.H >> 3, kBlock * VPT);
+    const int64_t S = (int64_t)a.P * a.T;
+    hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, NT_OUT>), dim3((unsigned)grid_for(S * nchunk)),
+                       dim3(kBlock), 0, s, a, nchunk);
     return hipGetLastError();
 }
 
 hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s)
 {
-    hipLaunchKernelGGL(combine_bf16_kernel, dim3(grid_for((int64_t)a.P * a.T)), dim3(kBlock), 0, s, a);
-    return hipGetLastError();
+    const int64_t out_bytes = (int64_t)a.P * a.T * a.H * 2;
+    if (out_bytes >= MOE_EP_COMBINE_LARGE_BYTES)
+        return launch_combine_shape<MOE_EP_COMBINE_LARGE>(a, s);
+    return launch_combine_shape<MOE_EP_COMBINE_SMALL>(a, s);
 }
 
 hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s)
 {
-    const dim3 grid(grid_for((int64_t)a.P * a.T));
+    const dim3 grid((unsigned)grid_for((int64_t)a.P * a.T));
     hipLaunchKernelGGL(combine_fp8_quant_kernel, grid, dim3(kBlock), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

@@ -72,11 +72,11 @@ class Plane(C.Structure):
                 ("out_rank_stride", C.c_int64), ("row_bytes", C.c_int64)]
 
 
-def _load():
-    if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run combine_route_mask_amd.build.build() "
+def _load(path: str = LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is not built; run combine_route_mask_amd.build.build() "
                           "(or __graft_entry__.build())")
-    L = C.CDLL(LIB_PATH)
+    L = C.CDLL(path)
     vp, i32, i64 = C.c_void_p, C.c_int32, C.c_int64
     L.moe_ep_is_supported.argtypes = []
     L.moe_ep_is_supported.restype = C.c_int
