@@ -40,6 +40,7 @@ WORKLOADS = {
     "ep8-mxfp8": W.EP8_MXFP8,
     "ep64": W.EP64_BF16,
     "ep64-nvfp4": W.EP64_NVFP4,
+    "agrs": W.AGRS16,
 }
 
 
@@ -128,6 +129,58 @@ class Setup:
         del self.eo, self.payload, self.ex, self.views
 
 
+class AgRsSetup:
+    """All-gatherv of [hidden, topk_weights, topk_ids] then reduce-scatterv of
+    the hidden partials over P virtual ranks, through the raw C ABI."""
+
+    def __init__(self, w):
+        import ctypes as C
+        import torch
+        from combine_route_mask_amd import moe_ep
+        self.w = w
+        d = W.draw_agrs_inputs(w, device="cuda")
+        self.sizes = d.sizes
+        total = int(d.sizes.sum())
+        self.N = total
+        self.hidden = d.hidden
+        self.wts = torch.from_numpy(d.weights).cuda()
+        self.ids_t = torch.from_numpy(d.ids).cuda()
+        self.outs = [torch.empty((w.P, total, w.H), dtype=torch.bfloat16, device="cuda"),
+                     torch.empty((w.P, total, w.k), dtype=torch.float32, device="cuda"),
+                     torch.empty((w.P, total, w.k), dtype=torch.int32, device="cuda")]
+        self.part = d.partial.contiguous()
+        self.rs_out = torch.empty((w.P, int(d.sizes.max()), w.H), dtype=torch.bfloat16, device="cuda")
+        # one checked call of each through the binding, then raw pointers
+        moe_ep.allgatherv(self.sizes.tolist(), [self.hidden, self.wts, self.ids_t], self.outs)
+        moe_ep.reduce_scatterv(self.sizes.tolist(), self.part, self.rs_out)
+        planes = []
+        for x, o in zip([self.hidden, self.wts, self.ids_t], self.outs):
+            planes.append(moe_ep.Plane(x.data_ptr(), x.stride(0) * x.element_size(), o.data_ptr(),
+                                       o.stride(0) * o.element_size(), x[0, 0].numel() * x.element_size()))
+        self._lib = moe_ep.lib
+        self._planes = (moe_ep.Plane * 3)(*planes)
+        self._sizes = (C.c_int32 * w.P)(*self.sizes.tolist())
+        self._rs = (C.c_void_p(self.part.data_ptr()), C.c_int64(self.part.stride(0) * 2),
+                    C.c_void_p(self.rs_out.data_ptr()), C.c_int64(self.rs_out.stride(0) * 2))
+        rowb = w.H * 2 + 8 * w.k
+        self.bytes = {"allgatherv": total * rowb * (1 + w.P), "reduce_scatterv": total * 2 * w.H * (w.P + 1)}
+
+    def dispatch(self):
+        import torch
+        st = torch.cuda.current_stream().cuda_stream
+        if self._lib.moe_ep_allgatherv(self.w.P, self._sizes, 3, self._planes, st):
+            raise RuntimeError(self._lib.moe_ep_last_error().decode())
+
+    def combine(self):
+        import torch
+        st = torch.cuda.current_stream().cuda_stream
+        if self._lib.moe_ep_reduce_scatterv(self.w.P, self._sizes, self.w.H, *self._rs, st):
+            raise RuntimeError(self._lib.moe_ep_last_error().decode())
+
+    def free(self):
+        del self.hidden, self.outs, self.part, self.rs_out
+
+
 def _graph(fn, reps=1):
     import torch
     g = torch.cuda.CUDAGraph()
@@ -157,7 +210,7 @@ def _time(fn, iters):
     return a.elapsed_time(b)
 
 
-def measure(setup, steps, warmup, flush_bytes=0):
+def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     """Step time of `steps` dispatch+combine steps after `warmup` untimed
     ones, eager (two C-ABI launches per step) and as one HIP-graph replay
     per step; per-launch kernel times from graphs of 20 back-to-back
@@ -171,13 +224,19 @@ def measure(setup, steps, warmup, flush_bytes=0):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    # the step's receive counts must match the host-side pair count
-    got_M = int(setup.views["counts"].sum().item())
-    assert got_M == setup.M, (got_M, setup.M)
-    ref_out = setup.out.clone()
-    ref_ids = setup.views["ids"].clone()
+    exchange = isinstance(setup, Setup) and check
+    if exchange:
+        # the step's receive counts must match the host-side pair count
+        got_M = int(setup.views["counts"].sum().item())
+        assert got_M == setup.M, (got_M, setup.M)
+        ref_out = setup.out.clone()
+        ref_ids = setup.views["ids"].clone()
 
     eager_ms = _time(step, steps) / steps
+    if not graphs:
+        return {"ms_per_step": eager_ms, "eager_ms_per_step": eager_ms,
+                "dispatch_ms": _time(setup.dispatch, steps) / steps,
+                "combine_ms": _time(setup.combine, steps) / steps, "wall_s": 0.0}
     # one graph holds `per` consecutive steps, so a small step is not bound
     # by the host's graph-launch rate; `steps` is rounded up to a multiple
     per = 1 if flush_bytes else 10
@@ -204,8 +263,9 @@ def measure(setup, steps, warmup, flush_bytes=0):
         graph_ms = _time(g_step.replay, replays) / (replays * per)
     wall = time.perf_counter() - wall0
     # graph replays must reproduce the eager step bit for bit
-    assert torch.equal(setup.out.view(torch.int16), ref_out.view(torch.int16))
-    assert torch.equal(setup.views["ids"], ref_ids)
+    if exchange:
+        assert torch.equal(setup.out.view(torch.int16), ref_out.view(torch.int16))
+        assert torch.equal(setup.views["ids"], ref_ids)
 
     reps = 20
     g_d = _graph(setup.dispatch, reps)
@@ -237,6 +297,18 @@ def calibrate(nbytes=2 << 30, iters=10):
 
 
 def summarize(setup, m):
+    if isinstance(setup, AgRsSetup):
+        b = setup.bytes
+        tot = b["allgatherv"] + b["reduce_scatterv"]
+        step_s = m["ms_per_step"] / 1e3
+        res = {"workload": setup.w.name, "rows": setup.N, "rows_per_s": setup.N / step_s,
+               "ms_per_step": m["ms_per_step"], "eager_ms_per_step": m["eager_ms_per_step"],
+               "step_bytes": tot, "step_GBps": tot / step_s / 1e9,
+               "allgatherv_ms": m["dispatch_ms"], "reduce_scatterv_ms": m["combine_ms"],
+               "allgatherv_GBps": b["allgatherv"] / (m["dispatch_ms"] / 1e3) / 1e9,
+               "reduce_scatterv_GBps": b["reduce_scatterv"] / (m["combine_ms"] / 1e3) / 1e9}
+        res["step_frac_of_peak"] = res["step_GBps"] / HBM_PEAK_GBS
+        return res, b
     w, N, M = setup.w, setup.N, setup.M
     b = step_bytes(w, N, M)
     step_s = m["ms_per_step"] / 1e3
@@ -290,7 +362,10 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ep8", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="ep64", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--also", default="ep64,ep8-mxfp8,agrs",
+                    help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--cold", action="store_true", help="flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
@@ -310,7 +385,8 @@ def main():
     calib = calibrate()
     print(f"[bench] setting up {w.name}", file=sys.stderr, flush=True)
     setup = Setup(w)
-    m = measure(setup, args.steps, args.warmup, flush_bytes=(1 << 30) if args.cold else 0)
+    m = measure(setup, args.steps, args.warmup, flush_bytes=(1 << 30) if args.cold else 0,
+                graphs=not args.no_graph)
     res, b = summarize(setup, m)
     setup.free()
     torch.cuda.empty_cache()
@@ -335,9 +411,9 @@ def main():
             continue
         wa = WORKLOADS[name]
         print(f"[bench] setting up {wa.name}", file=sys.stderr, flush=True)
-        sa = Setup(wa)
+        sa = AgRsSetup(wa) if name == "agrs" else Setup(wa)
         ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2),
-                     flush_bytes=(1 << 30) if args.cold else 0)
+                     flush_bytes=(1 << 30) if args.cold else 0, graphs=not args.no_graph)
         ra, _ = summarize(sa, ma)
         sa.free()
         del sa

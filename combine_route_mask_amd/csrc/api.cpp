@@ -272,6 +272,10 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
     a.k = p.top_k;
     a.E = p.num_experts;
     a.epr = p.num_experts / p.ep_size;
+    a.epr_shift = -1;
+    for (int sh = 0; sh < 31; ++sh)
+        if ((1 << sh) == a.epr)
+            a.epr_shift = sh;
     a.invalid_id = p.invalid_expert_id;
     for (int s = 0; s < p.ep_size; ++s)
         a.n[s] = num_tokens[s];

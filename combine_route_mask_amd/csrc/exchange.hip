@@ -49,9 +49,13 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kScanUnroll = 4;          // 256-slot chunks per scan step
+#ifndef MOE_EP_SCAN_UNROLL
+#define MOE_EP_SCAN_UNROLL 2
+#endif
+constexpr int kScanUnroll = MOE_EP_SCAN_UNROLL; // 256-slot chunks per scan step
 constexpr int kWaves = kBlock / 64;
 constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
+constexpr int kPlaneGroup = 8;          // destinations per id-plane item
 constexpr int kDVpt = MOE_EP_DISPATCH_VPT;
 constexpr int kDChunk = kBlock * kDVpt; // 16-byte vectors per dispatch row chunk
 
@@ -69,29 +73,46 @@ __device__ __forceinline__ void store16(void *p, u32x4 v)
 #endif
 }
 
-// Destination-rank mask of one token: bit r set when one of its k ids is an
-// expert of rank r (experts e / epr == r).  OR-ing the bits deduplicates
-// tokens with several experts on one rank; ids outside [0, E) set nothing.
-// For k <= 16 all k loads are issued before the first is used.
-__device__ __forceinline__ uint64_t route_mask(const int32_t *__restrict__ idrow, int k, int E,
-                                               int epr)
+// Bit of the rank owning expert id (experts are owned in contiguous blocks
+// of epr), or 0 for an id outside [0, E).
+__device__ __forceinline__ uint64_t owner_bit(const DispatchArgs &a, int id)
 {
+    if ((unsigned)id >= (unsigned)a.E)
+        return 0ull;
+    const unsigned r = a.epr_shift >= 0 ? (unsigned)id >> a.epr_shift : (unsigned)id / (unsigned)a.epr;
+    return 1ull << r;
+}
+
+// Destination-rank mask of token q: bit r set when one of its k ids is an
+// expert of rank r.  OR-ing the bits deduplicates tokens with several
+// experts on one rank.  KQ > 0: the k = 4*KQ ids are read as KQ 16-byte
+// vectors; KQ == 0: any k, all loads of the first 16 ids issued together.
+template <int KQ>
+__device__ __forceinline__ uint64_t route_mask(const DispatchArgs &a, int64_t q)
+{
+    const int32_t *__restrict__ idrow = a.ids + q * a.k;
     uint64_t m = 0;
-    if (k <= 16) {
+    if constexpr (KQ > 0) {
+        u32x4 v[KQ];
+#pragma unroll
+        for (int j = 0; j < KQ; ++j)
+            v[j] = reinterpret_cast<const u32x4 *>(idrow)[j];
+#pragma unroll
+        for (int j = 0; j < KQ; ++j)
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                m |= owner_bit(a, (int)v[j][e]);
+    } else if (a.k <= 16) {
         int32_t id[16];
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            id[j] = j < k ? idrow[j] : -1;
+            id[j] = j < a.k ? idrow[j] : -1;
 #pragma unroll
         for (int j = 0; j < 16; ++j)
-            if (id[j] >= 0 && id[j] < E)
-                m |= 1ull << (unsigned)(id[j] / epr);
-        return m;
-    }
-    for (int j = 0; j < k; ++j) {
-        const int id = idrow[j];
-        if (id >= 0 && id < E)
-            m |= 1ull << (unsigned)(id / epr);
+            m |= owner_bit(a, id[j]);
+    } else {
+        for (int j = 0; j < a.k; ++j)
+            m |= owner_bit(a, idrow[j]);
     }
     return m;
 }
@@ -136,11 +157,13 @@ __device__ __forceinline__ void copy_row_any(const uint8_t *src, int64_t nbytes,
 }
 
 // Receive bookkeeping of destination rank r: walks every source slot q in
-// ascending order, 1024 slots per step; a wave ballot marks the slots whose
-// token goes to r, v_mbcnt gives each one its rank inside the wave, and the
-// per-wave totals in LDS give the step's exclusive prefix.  Produces the
-// ascending list of valid slots, the per-source counts and their exclusive
-// prefix (src_offsets[P] = rows received).
+// ascending order, 1024 slots per step (four per lane, all id rows loaded
+// before any is tested); a wave ballot marks the slots whose token goes to
+// r, v_mbcnt gives each one its rank inside the wave, and the per-wave
+// totals in LDS give the step's exclusive prefix.  Produces the ascending
+// list of valid slots, the per-source counts and their exclusive prefix
+// (src_offsets[P] = rows received).
+template <int KQ>
 __device__ void scan_destination(const DispatchArgs &a, int r)
 {
     __shared__ int wave_tot[kScanUnroll][kWaves];
@@ -149,13 +172,16 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
     uint8_t *region = a.ws + (int64_t)r * a.region;
     int32_t *slots = reinterpret_cast<int32_t *>(region + a.off_slots);
     const int64_t S = (int64_t)a.P * a.T;
+    const uint64_t rbit = 1ull << r;
+    const uint32_t lo = (uint32_t)(r * a.epr); // rank r owns experts [lo, lo + epr)
     int base = 0;
     for (int64_t c0 = 0; c0 < S; c0 += kBlock * kScanUnroll) {
-        int bit[kScanUnroll], src[kScanUnroll], tok[kScanUnroll];
+        bool live[kScanUnroll];
+        int src[kScanUnroll], tok[kScanUnroll];
 #pragma unroll
         for (int u = 0; u < kScanUnroll; ++u) {
             const int64_t q = c0 + u * kBlock + tid;
-            bit[u] = 0;
+            live[u] = false;
             src[u] = 0;
             tok[u] = -1;
             if (q < S) {
@@ -163,9 +189,34 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
                 const int t = (int)(q - (int64_t)s * a.T);
                 src[u] = s;
                 tok[u] = t;
-                if (t < a.n[s])
-                    bit[u] = (int)((route_mask(a.ids + q * a.k, a.k, a.E, a.epr) >> r) & 1u);
+                live[u] = t < a.n[s];
             }
+        }
+        int bit[kScanUnroll];
+        if constexpr (KQ > 0) {
+            u32x4 v[kScanUnroll][KQ];
+            const u32x4 none = {~0u, ~0u, ~0u, ~0u}; // ids that no rank owns
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u)
+#pragma unroll
+                for (int j = 0; j < KQ; ++j)
+                    v[u][j] = live[u] ? reinterpret_cast<const u32x4 *>(
+                                            a.ids + (c0 + u * kBlock + tid) * a.k)[j]
+                                      : none;
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u) {
+                bool hit = false;
+#pragma unroll
+                for (int j = 0; j < KQ; ++j)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        hit |= v[u][j][e] - lo < (uint32_t)a.epr;
+                bit[u] = live[u] && hit;
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < kScanUnroll; ++u)
+                bit[u] = live[u] && (route_mask<0>(a, c0 + u * kBlock + tid) & rbit);
         }
         uint64_t bal[kScanUnroll];
 #pragma unroll
@@ -207,14 +258,17 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
     }
 }
 
-// Id and weight planes of destination r for slots [c*kPlaneSlots, ...), in
-// two phases.  First each thread computes one slot's destination mask into
-// LDS (the items of destination 0 also store every token's mask in its
-// source rank's region, for combine).  Then the block walks the chunk's
-// k-word id rows word by word, four words per thread in flight, so
-// consecutive lanes write consecutive words: a slot whose token goes to r
-// gets the token's ids and weights, every other slot k copies of invalid_id.
-__device__ void write_id_planes(const DispatchArgs &a, int r, int64_t c)
+// Id and weight planes of destinations [r0, r1) for slots
+// [c*kPlaneSlots, ...), in two phases.  First each lane computes one slot's
+// destination mask into LDS (the items of the first destination group also
+// store every token's mask in its source rank's region, for combine).  Then
+// the block walks the chunk's id rows in 16-byte units (KQ > 0) or words,
+// each unit read once (only for tokens that go somewhere) and stored to
+// every destination of the group: a slot whose token goes to r gets the
+// token's ids and weights, every other slot k copies of invalid_id.
+// Consecutive lanes write consecutive units.
+template <int KQ>
+__device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c)
 {
     __shared__ uint64_t smask[kPlaneSlots];
     const int64_t S = (int64_t)a.P * a.T;
@@ -224,38 +278,46 @@ __device__ void write_id_planes(const DispatchArgs &a, int r, int64_t c)
         const int64_t q = q0 + threadIdx.x;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
-        const uint64_t mask = t < a.n[s] ? route_mask(a.ids + q * a.k, a.k, a.E, a.epr) : 0ull;
+        const uint64_t mask = t < a.n[s] ? route_mask<KQ>(a, q) : 0ull;
         smask[threadIdx.x] = mask;
-        if (r == 0)
+        if (r0 == 0)
             *reinterpret_cast<uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks +
                                           (int64_t)t * 8) = mask;
     }
     __syncthreads();
-    uint8_t *reg = a.ws + (int64_t)r * a.region;
-    int32_t *__restrict__ ids_out = reinterpret_cast<int32_t *>(reg + a.off_ids) + q0 * a.k;
-    float *__restrict__ w_out = reinterpret_cast<float *>(reg + a.off_weights) + q0 * a.k;
-    const int32_t *__restrict__ ids_in = a.ids + q0 * a.k;
-    const float *__restrict__ w_in = a.weights ? a.weights + q0 * a.k : nullptr;
-    const int nwords = nslot * a.k;
-    constexpr int U = 4;
-    for (int e0 = threadIdx.x; e0 < nwords; e0 += U * kBlock) {
-        int32_t idv[U];
-        float wv[U];
-        bool go[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int e = e0 + u * kBlock;
-            go[u] = e < nwords && ((smask[e / a.k] >> r) & 1u);
-            idv[u] = go[u] ? ids_in[e] : a.invalid_id;
-            wv[u] = (go[u] && w_in) ? w_in[e] : 0.0f;
+    if constexpr (KQ > 0) {
+        const u32x4 *__restrict__ ids_in = reinterpret_cast<const u32x4 *>(a.ids) + q0 * KQ;
+        const u32x4 *__restrict__ w_in =
+            a.weights ? reinterpret_cast<const u32x4 *>(a.weights) + q0 * KQ : nullptr;
+        const uint32_t inv = (uint32_t)a.invalid_id;
+        const u32x4 marker = {inv, inv, inv, inv};
+        const int nunits = nslot * KQ;
+        for (int e = threadIdx.x; e < nunits; e += kBlock) {
+            const uint64_t mk = smask[e / KQ];
+            const u32x4 idv = mk ? ids_in[e] : marker;
+            const u32x4 wv = (mk && w_in) ? w_in[e] : marker;
+            for (int r = r0; r < r1; ++r) {
+                uint8_t *reg = a.ws + (int64_t)r * a.region;
+                const bool go = (mk >> r) & 1u;
+                reinterpret_cast<u32x4 *>(reg + a.off_ids)[q0 * KQ + e] = go ? idv : marker;
+                if (go && w_in)
+                    reinterpret_cast<u32x4 *>(reg + a.off_weights)[q0 * KQ + e] = wv;
+            }
         }
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-            const int e = e0 + u * kBlock;
-            if (e < nwords) {
-                ids_out[e] = idv[u];
-                if (go[u] && w_in)
-                    w_out[e] = wv[u];
+    } else {
+        const int32_t *__restrict__ ids_in = a.ids + q0 * a.k;
+        const float *__restrict__ w_in = a.weights ? a.weights + q0 * a.k : nullptr;
+        const int nwords = nslot * a.k;
+        for (int e = threadIdx.x; e < nwords; e += kBlock) {
+            const uint64_t mk = smask[e / a.k];
+            const int32_t idv = mk ? ids_in[e] : a.invalid_id;
+            const float wv = (mk && w_in) ? w_in[e] : 0.0f;
+            for (int r = r0; r < r1; ++r) {
+                uint8_t *reg = a.ws + (int64_t)r * a.region;
+                const bool go = (mk >> r) & 1u;
+                reinterpret_cast<int32_t *>(reg + a.off_ids)[q0 * a.k + e] = go ? idv : a.invalid_id;
+                if (go && w_in)
+                    reinterpret_cast<float *>(reg + a.off_weights)[q0 * a.k + e] = wv;
             }
         }
     }
@@ -265,13 +327,14 @@ __device__ void write_id_planes(const DispatchArgs &a, int r, int64_t c)
 // Chunk c of token q's payload row (kDVpt 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
 // chunk 0 also carries the scale row.
+template <int KQ>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
     const int t = (int)(q - (int64_t)s * a.T);
     if (t >= a.n[s])
         return;
-    const uint64_t mask = route_mask(a.ids + q * a.k, a.k, a.E, a.epr);
+    const uint64_t mask = route_mask<KQ>(a, q);
     if (!mask)
         return;
     const int64_t nvec = a.row_bytes >> 4;
@@ -304,28 +367,32 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 
 // One launch, three block roles touching disjoint memory:
 //   [0, P)                    receive bookkeeping of destination r
-//   [P, P + plane_blocks)     id / weight planes, (r, slot chunk) items
+//   [P, P + plane_blocks)     id / weight planes, (destination group, slot chunk) items
 //   [P + plane_blocks, grid)  payload scatter, (token, row chunk) items
 // The last two roles loop over their items when there are more items than
-// blocks.
+// blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k).
+template <int KQ>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
 {
     const int64_t b = blockIdx.x;
     if (b < a.P) {
-        scan_destination(a, (int)b);
+        scan_destination<KQ>(a, (int)b);
         return;
     }
     if (b < a.P + plane_blocks) {
-        for (int64_t w = b - a.P; w < (int64_t)a.P * nplane; w += plane_blocks)
-            write_id_planes(a, (int)(w / nplane), w % nplane);
+        const int ngroups = (a.P + kPlaneGroup - 1) / kPlaneGroup;
+        for (int64_t w = b - a.P; w < (int64_t)ngroups * nplane; w += plane_blocks) {
+            const int g = (int)(w / nplane);
+            write_id_planes<KQ>(a, g * kPlaneGroup, min(a.P, (g + 1) * kPlaneGroup), w % nplane);
+        }
         return;
     }
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t first = a.P + plane_blocks;
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
-        scatter_chunk(a, w / nchunk, w % nchunk);
+        scatter_chunk<KQ>(a, w / nchunk, w % nchunk);
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
@@ -578,16 +645,32 @@ inline int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 } // namespace
 
-hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s)
+template <int KQ>
+static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t nplane = ceil_div(S, kPlaneSlots);
-    const int64_t plane_blocks = grid_for((int64_t)a.P * nplane);
+    const int64_t plane_blocks = grid_for(ceil_div(a.P, kPlaneGroup) * nplane);
     const int64_t nchunk = ceil_div(a.row_bytes >> 4, kDChunk);
-    const int64_t grid = a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
-    hipLaunchKernelGGL(dispatch_kernel, dim3((unsigned)grid), dim3(kBlock), 0, s, a, nplane,
+    const int64_t grid =
+        a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
+    hipLaunchKernelGGL(dispatch_kernel<KQ>, dim3((unsigned)grid), dim3(kBlock), 0, s, a, nplane,
                        plane_blocks, nchunk);
     return hipGetLastError();
+}
+
+hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s)
+{
+    // id rows of 4, 8 or 16 ids with 16-byte aligned id / weight planes move
+    // as 16-byte vectors; anything else takes the word path
+    const bool al = ((uintptr_t)a.ids & 15) == 0 && ((uintptr_t)a.weights & 15) == 0;
+    if (al && a.k == 8)
+        return launch_dispatch_kq<2>(a, s);
+    if (al && a.k == 4)
+        return launch_dispatch_kq<1>(a, s);
+    if (al && a.k == 16)
+        return launch_dispatch_kq<4>(a, s);
+    return launch_dispatch_kq<0>(a, s);
 }
 
 template <int VPT, int G, bool NT_OUT>

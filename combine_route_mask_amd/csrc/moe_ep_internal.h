@@ -33,6 +33,7 @@ struct DispatchArgs {
         off_src_offsets, off_masks;
     int64_t row_bytes, srow_bytes;
     int32_t P, T, k, E, epr, invalid_id;
+    int32_t epr_shift;               // log2(epr) when epr is a power of two, else -1
     int32_t n[MOE_EP_MAX_RANKS];     // local token counts
 };
 
