@@ -34,6 +34,78 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_ep8_bf16.txt")
+KERNEL_SOURCE = os.path.join(ROOT, "combine_route_mask_amd", "csrc", "exchange.hip")
+
+
+def source_digest() -> str:
+    import hashlib
+    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+
+
+def measured_traffic(kernel: str, workload: str):
+    """HBM bytes per launch of `kernel` on `workload` from the committed
+    counter summary, or None when there is none or the kernel source has
+    changed since the counters were taken."""
+    try:
+        rows = [json.loads(l) for l in open(TRAFFIC_SUMMARY) if l.startswith("{")]
+    except OSError:
+        return None
+    for r in rows:
+        if r.get("kernel") == kernel and r.get("workload") == workload and \
+                r.get("source_digest") == source_digest():
+            return r["hbm_bytes_per_launch"]
+    return None
+
+
+def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str):
+    """Per-launch HBM traffic from two counter runs (FETCH_SIZE, WRITE_SIZE;
+    KiB per dispatch).  Each counter is scaled by what it reads for the
+    calibration copy kernel of known size (2 GiB read + 2 GiB written)."""
+    import csv
+    import collections
+
+    def load(path):
+        per = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"]
+            key = name.split("(anonymous namespace)::")[-1].split("(")[0] if "moe_ep" in name else name
+            per[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_csv), load(write_csv)
+    copy_kib = (2 << 30) / 1024
+    cf = [v for (k, g), vs in fetch.items() if "copyBuffer" in k for v in vs if v > copy_kib / 4]
+    cw = [v for (k, g), vs in write.items() if "copyBuffer" in k for v in vs if v > copy_kib / 2]
+    f_scale = copy_kib / (sum(cf) / len(cf))
+    w_scale = copy_kib / (sum(cw) / len(cw))
+    lines = []
+    for (k, g), vs in sorted(fetch.items()):
+        if "moe_ep" not in k and not k.startswith(("dispatch_kernel", "combine_")):
+            continue
+        wv = write.get((k, g), [0.0])
+        fk, wk = sum(vs) / len(vs), sum(wv) / len(wv)
+        lines.append(json.dumps({
+            "kernel": k.split("<")[0], "instance": k, "workload": workload, "grid_threads": g,
+            "fetch_KiB": round(fk, 1), "write_KiB": round(wk, 1),
+            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+            "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
+            "launches": len(vs), "source_digest": source_digest()}))
+    with open(out_path, "w") as f:
+        f.write("# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE in KiB per\n"
+                "# dispatch), each scaled by its reading for a plain 2 GiB device copy\n"
+                "# (calibration copy in bench.py: 2 GiB read, 2 GiB written).  Commands, run from /tmp\n"
+                "# with TMPDIR=/tmp:\n"
+                "#   rocprofv3 --pmc FETCH_SIZE -d <repo>/gpurun_out/pmc_fetch -o pmc --output-format csv -- \\\n"
+                "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
+                "#   rocprofv3 --pmc WRITE_SIZE -d <repo>/gpurun_out/pmc_write -o pmc --output-format csv -- \\\n"
+                "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
+                "#   python3 <repo>/bench.py --pmc-summary <repo>/gpurun_out/pmc_fetch/pmc_counter_collection.csv \\\n"
+                "#       <repo>/gpurun_out/pmc_write/pmc_counter_collection.csv\n"
+                "# source_digest: first 16 hex digits of sha256(combine_route_mask_amd/csrc/exchange.hip)\n")
+        for l in lines:
+            f.write(l + "\n")
+    return lines
 
 WORKLOADS = {
     "ep8": W.EP8_BF16,
@@ -369,7 +441,13 @@ def main():
     ap.add_argument("--cold", action="store_true", help="flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the counter traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        for l in pmc_summary(*args.pmc_summary, TRAFFIC_SUMMARY, WORKLOADS[args.config].name):
+            print(l)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this exchange runs P virtual EP ranks on one GPU; "
                                    "--gpus above 1 is not supported"}))
@@ -400,8 +478,9 @@ def main():
         dom_name, dom_ms, dom_bytes = ("dispatch_kernel", m["dispatch_ms"], b["dispatch"]) \
             if m["dispatch_ms"] >= m["combine_ms"] else ("combine_bf16_kernel", m["combine_ms"], b["combine"])
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
+    traffic = measured_traffic(dom_name, w.name)
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
                 "frac_of_measured_copy": achieved / calib["copy_GBps"]}
 

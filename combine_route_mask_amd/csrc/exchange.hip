@@ -40,6 +40,9 @@
 #ifndef MOE_EP_COMBINE_LARGE
 #define MOE_EP_COMBINE_LARGE 4, 2, 1
 #endif
+#ifndef MOE_EP_FP8_GATHER
+#define MOE_EP_FP8_GATHER 4 // ranks per round in the FP8 combine kernels
+#endif
 #ifndef MOE_EP_COMBINE_LARGE_BYTES
 #define MOE_EP_COMBINE_LARGE_BYTES (128ll << 20)
 #endif
@@ -503,133 +506,173 @@ __device__ __forceinline__ float scale_pow2(uint32_t xb, int e)
     return __uint_as_float(sign | ((uint32_t)ev << 23) | (mant << 16));
 }
 
-// FP8 combine, sending side: every rank r that holds token (s, t) quantises
-// its row q = s*T + t (e4m3fn, one e8m0 scale per 32 elements) into source
-// rank s's landing plane at slot r*T + t.  A thread handles 16 elements;
-// two neighbouring lanes share a 32-element block and its amax.
-__global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a)
+// e4m3 codes and e8m0 scale code of one 16-element half of a 32-element
+// block (the two halves sit in neighbouring lanes, which exchange their
+// amax); a block holding a NaN or an infinity gets scale 0xFF, codes 0x7F.
+// All lanes of the wave must call this together (lane shuffle).
+__device__ __forceinline__ void quantise16(u32x4 x0, u32x4 x1, u32x4 &codes, uint32_t &scale_code)
+{
+    const uint32_t w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        amax = max(amax, w[e] & 0x7FFFu);
+        amax = max(amax, (w[e] >> 16) & 0x7FFFu);
+    }
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+    uint32_t c[16];
+    if (amax >= 0x7F80u) {
+        scale_code = 0xFFu;
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+            c[e] = 0x7Fu;
+    } else {
+        const int ex = fp8_block_exponent(amax);
+        scale_code = (uint32_t)(ex + 127);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            c[2 * e] = f32_to_e4m3(scale_pow2(w[e] & 0xFFFFu, ex));
+            c[2 * e + 1] = f32_to_e4m3(scale_pow2(w[e] >> 16, ex));
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        codes[j] = c[4 * j] | (c[4 * j + 1] << 8) | (c[4 * j + 2] << 16) | (c[4 * j + 3] << 24);
+}
+
+// FP8 combine, sending side: item (token q = s*T + t, chunk c of 256
+// 16-element groups).  Every rank r that holds the token quantises its row
+// q (e4m3fn, one e8m0 scale per 32 elements) into source rank s's landing
+// plane at slot r*T + t; the rows of up to G ranks are loaded before any is
+// quantised.  Each lane owns one 16-element group; lane pairs share a block.
+template <int G>
+__global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
-    const int64_t rank_stride = S * a.H;
+    const int64_t rank_bytes = S * a.H * 2;
     const int64_t ngroups = a.H >> 4;
-    for (int64_t q = blockIdx.x; q < S; q += gridDim.x) {
+    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
+        const int64_t q = w / nchunk, c = w % nchunk;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
         if (t >= a.n[s])
             continue;
+        const int64_t g = c * kBlock + threadIdx.x;
+        const bool act = g < ngroups; // ngroups and kBlock even: lane pairs agree
         uint8_t *land = a.ws + (int64_t)s * a.region;
         const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2 + g * 32;
         uint64_t m = mask;
         while (m) {
-            const int r = __builtin_ctzll(m);
-            m &= m - 1;
-            const uint4 *src = reinterpret_cast<const uint4 *>(a.eo + r * rank_stride + q * a.H);
-            const int64_t slot = (int64_t)r * a.T + t;
-            uint4 *codes = reinterpret_cast<uint4 *>(land + a.off_land_codes + slot * a.H);
-            uint8_t *scales = land + a.off_land_scales + slot * (a.H >> 5);
-            for (int64_t g0 = 0; g0 < ngroups; g0 += kBlock) {
-                const int64_t g = g0 + threadIdx.x;
-                const bool act = g < ngroups; // ngroups even: lane pairs agree
-                uint4 x0 = {0, 0, 0, 0}, x1 = {0, 0, 0, 0};
+            int r[G];
+            int cnt = 0;
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                r[u] = 0;
+                if (m) {
+                    r[u] = __builtin_ctzll(m);
+                    m &= m - 1;
+                    cnt = u + 1;
+                }
+            }
+            u32x4 x[G][2];
+#pragma unroll
+            for (int u = 0; u < G; ++u)
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    x[u][h] = (act && u < cnt)
+                                  ? load16_nt(src + (int64_t)r[u] * rank_bytes + h * 16)
+                                  : u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                if (u >= cnt)
+                    break;
+                u32x4 codes;
+                uint32_t sc;
+                quantise16(x[u][0], x[u][1], codes, sc);
                 if (act) {
-                    x0 = src[2 * g];
-                    x1 = src[2 * g + 1];
+                    const int64_t slot = (int64_t)r[u] * a.T + t;
+                    *reinterpret_cast<u32x4 *>(land + a.off_land_codes + slot * a.H + g * 16) = codes;
+                    if ((g & 1) == 0)
+                        land[a.off_land_scales + slot * (a.H >> 5) + (g >> 1)] = (uint8_t)sc;
                 }
-                const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-                uint32_t amax = 0;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    amax = max(amax, w[e] & 0x7FFFu);
-                    amax = max(amax, (w[e] >> 16) & 0x7FFFu);
-                }
-                amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-                if (!act)
-                    continue;
-                uint32_t c[16];
-                uint32_t scale_code;
-                if (amax >= 0x7F80u) {   // a NaN or an infinity in the block
-                    scale_code = 0xFFu;
-#pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        c[e] = 0x7Fu;
-                } else {
-                    const int ex = fp8_block_exponent(amax);
-                    scale_code = (uint32_t)(ex + 127);
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        c[2 * e] = f32_to_e4m3(scale_pow2(w[e] & 0xFFFFu, ex));
-                        c[2 * e + 1] = f32_to_e4m3(scale_pow2(w[e] >> 16, ex));
-                    }
-                }
-                uint4 o;
-                o.x = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
-                o.y = c[4] | (c[5] << 8) | (c[6] << 16) | (c[7] << 24);
-                o.z = c[8] | (c[9] << 8) | (c[10] << 16) | (c[11] << 24);
-                o.w = c[12] | (c[13] << 8) | (c[14] << 16) | (c[15] << 24);
-                codes[g] = o;
-                if ((g & 1) == 0)
-                    scales[g >> 1] = (uint8_t)scale_code;
             }
         }
     }
 }
 
-// FP8 combine, receiving side: source token (s, t) dequantises the landing
-// rows r*T + t of every rank r in its mask, sums them in fp32 (ascending r)
-// and rounds to bf16.
-__global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs a)
+// FP8 combine, receiving side: item (token q = s*T + t, chunk c of 256
+// 16-element groups).  Each lane dequantises its group of the landing rows
+// r*T + t of every rank r in the token's mask (codes of up to G ranks loaded
+// at once), sums them in fp32 in ascending rank order and rounds to bf16.
+template <int G>
+__global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t ngroups = a.H >> 4;
-    for (int64_t q = blockIdx.x; q < S; q += gridDim.x) {
+    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
+        const int64_t q = w / nchunk, c = w % nchunk;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
-        if (t >= a.n[s])
+        const int64_t g = c * kBlock + threadIdx.x;
+        if (t >= a.n[s] || g >= ngroups)
             continue;
         const uint8_t *land = a.ws + (int64_t)s * a.region;
         const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
-        uint4 *dst = reinterpret_cast<uint4 *>(a.out + q * a.H);
-        for (int64_t g0 = 0; g0 < ngroups; g0 += kBlock) {
-            const int64_t g = g0 + threadIdx.x;
-            if (g >= ngroups)
-                break;
-            float acc[16];
+        float acc[16];
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                acc[e] = 0.0f;
-            uint64_t m = mask;
-            while (m) {
-                const int r = __builtin_ctzll(m);
-                m &= m - 1;
-                const int64_t slot = (int64_t)r * a.T + t;
-                const uint4 cv = reinterpret_cast<const uint4 *>(land + a.off_land_codes + slot * a.H)[g];
-                const uint32_t sc = land[a.off_land_scales + slot * (a.H >> 5) + (g >> 1)];
-                const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
-                if (sc == 0xFFu) {
+        for (int e = 0; e < 16; ++e)
+            acc[e] = 0.0f;
+        uint64_t m = mask;
+        while (m) {
+            int r[G];
+            int cnt = 0;
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                r[u] = 0;
+                if (m) {
+                    r[u] = __builtin_ctzll(m);
+                    m &= m - 1;
+                    cnt = u + 1;
+                }
+            }
+            u32x4 cv[G];
+            uint32_t sc[G];
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                if (u < cnt) {
+                    const int64_t slot = (int64_t)r[u] * a.T + t;
+                    cv[u] = load16_nt(land + a.off_land_codes + slot * a.H + g * 16);
+                    sc[u] = land[a.off_land_scales + slot * (a.H >> 5) + (g >> 1)];
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < G; ++u) {
+                if (u >= cnt)
+                    break;
+                if (sc[u] == 0xFFu) {
 #pragma unroll
                     for (int e = 0; e < 16; ++e)
                         acc[e] = __uint_as_float(0x7FC00000u);
                     continue;
                 }
-                const int ex = (int)sc - 127;
+                const int ex = (int)sc[u] - 127;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const uint32_t code = (cw[e >> 2] >> (8 * (e & 3))) & 0xFFu;
+                    const uint32_t code = (cv[u][e >> 2] >> (8 * (e & 3))) & 0xFFu;
                     acc[e] += __builtin_amdgcn_ldexpf(e4m3_to_f32(code), ex);
                 }
             }
-            uint4 o0, o1;
-            o0.x = pack_bf16x2(acc[0], acc[1]);
-            o0.y = pack_bf16x2(acc[2], acc[3]);
-            o0.z = pack_bf16x2(acc[4], acc[5]);
-            o0.w = pack_bf16x2(acc[6], acc[7]);
-            o1.x = pack_bf16x2(acc[8], acc[9]);
-            o1.y = pack_bf16x2(acc[10], acc[11]);
-            o1.z = pack_bf16x2(acc[12], acc[13]);
-            o1.w = pack_bf16x2(acc[14], acc[15]);
-            dst[2 * g] = o0;
-            dst[2 * g + 1] = o1;
         }
+        u32x4 o0, o1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            o0[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
+            o1[j] = pack_bf16x2(acc[8 + 2 * j], acc[8 + 2 * j + 1]);
+        }
+        u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + g * 16);
+        dst[0] = o0;
+        dst[1] = o1;
     }
 }
 
@@ -693,12 +736,13 @@ hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s)
 
 hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s)
 {
-    const dim3 grid((unsigned)grid_for((int64_t)a.P * a.T));
-    hipLaunchKernelGGL(combine_fp8_quant_kernel, grid, dim3(kBlock), 0, s, a);
+    const int64_t nchunk = ceil_div((int64_t)a.H >> 4, kBlock);
+    const dim3 grid((unsigned)grid_for((int64_t)a.P * a.T * nchunk));
+    hipLaunchKernelGGL(combine_fp8_quant_kernel<MOE_EP_FP8_GATHER>, grid, dim3(kBlock), 0, s, a, nchunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(combine_fp8_gather_kernel, grid, dim3(kBlock), 0, s, a);
+    hipLaunchKernelGGL(combine_fp8_gather_kernel<MOE_EP_FP8_GATHER>, grid, dim3(kBlock), 0, s, a, nchunk);
     return hipGetLastError();
 }
 
