@@ -41,7 +41,7 @@
 #define MOE_EP_COMBINE_LARGE 4, 2, 1
 #endif
 #ifndef MOE_EP_FP8_GATHER
-#define MOE_EP_FP8_GATHER 4 // ranks per round in the FP8 combine kernels
+#define MOE_EP_FP8_GATHER 2 // ranks per round in the FP8 combine kernels
 #endif
 #ifndef MOE_EP_COMBINE_LARGE_BYTES
 #define MOE_EP_COMBINE_LARGE_BYTES (128ll << 20)
@@ -51,6 +51,7 @@ namespace moe_ep {
 namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef MOE_EP_SCAN_UNROLL
 #define MOE_EP_SCAN_UNROLL 2
@@ -520,24 +521,26 @@ __device__ __forceinline__ void quantise16(u32x4 x0, u32x4 x1, u32x4 &codes, uin
         amax = max(amax, (w[e] >> 16) & 0x7FFFu);
     }
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
-    uint32_t c[16];
     if (amax >= 0x7F80u) {
         scale_code = 0xFFu;
-#pragma unroll
-        for (int e = 0; e < 16; ++e)
-            c[e] = 0x7Fu;
-    } else {
-        const int ex = fp8_block_exponent(amax);
-        scale_code = (uint32_t)(ex + 127);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            c[2 * e] = f32_to_e4m3(scale_pow2(w[e] & 0xFFFFu, ex));
-            c[2 * e + 1] = f32_to_e4m3(scale_pow2(w[e] >> 16, ex));
-        }
+        codes = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        return;
     }
+    const int ex = fp8_block_exponent(amax);
+    scale_code = (uint32_t)(ex + 127);
+    // x * 2^-ex is exact (integer exponent arithmetic) and within +-448, so
+    // the hardware e4m3 conversion (round to nearest even, no saturation
+    // reached) rounds it once; v_cvt_pk_fp8_f32 packs two codes, first
+    // operand in the lower byte, into the low or high half of a word.
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-        codes[j] = c[4 * j] | (c[4 * j + 1] << 8) | (c[4 * j + 2] << 16) | (c[4 * j + 3] << 24);
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(scale_pow2(w0 & 0xFFFFu, ex), scale_pow2(w0 >> 16, ex),
+                                                     0, false);
+        packed = __builtin_amdgcn_cvt_pk_fp8_f32(scale_pow2(w1 & 0xFFFFu, ex), scale_pow2(w1 >> 16, ex),
+                                                 packed, true);
+        codes[j] = (uint32_t)packed;
+    }
 }
 
 // FP8 combine, sending side: item (token q = s*T + t, chunk c of 256
@@ -657,10 +660,15 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs 
                     continue;
                 }
                 const int ex = (int)sc[u] - 127;
+                // v_cvt_pk_f32_fp8 decodes two codes (low byte first) exactly
 #pragma unroll
-                for (int e = 0; e < 16; ++e) {
-                    const uint32_t code = (cv[u][e >> 2] >> (8 * (e & 3))) & 0xFFu;
-                    acc[e] += __builtin_amdgcn_ldexpf(e4m3_to_f32(code), ex);
+                for (int j = 0; j < 4; ++j) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv[u][j], false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv[u][j], true);
+                    acc[4 * j] += __builtin_amdgcn_ldexpf(lo[0], ex);
+                    acc[4 * j + 1] += __builtin_amdgcn_ldexpf(lo[1], ex);
+                    acc[4 * j + 2] += __builtin_amdgcn_ldexpf(hi[0], ex);
+                    acc[4 * j + 3] += __builtin_amdgcn_ldexpf(hi[1], ex);
                 }
             }
         }
