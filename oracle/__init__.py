@@ -72,17 +72,17 @@ def _declare(L):
     L.orc_owner.restype = _i
     L.orc_token_goes_to.argtypes = [_p, _i, _i, _i, _i]
     L.orc_token_goes_to.restype = _i
-    L.orc_dispatch.argtypes = [_i, _i, _i, _i, C.c_int32, _p, _p, _i64, _p, _i64, _p, _p,
-                               _i, _i, _p, _p, _p, _p, _p, _p, _p]
+    L.orc_dispatch.argtypes = [_i, _i, _i, _i, C.c_int32, C.c_uint64, _p, _p, _i64, _p, _i64, _p,
+                               _p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
     L.orc_dispatch.restype = None
-    L.orc_combine_token_bf16.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p]
+    L.orc_combine_token_bf16.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _p, _p]
     L.orc_combine_token_bf16.restype = None
-    L.orc_combine_bf16.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p]
+    L.orc_combine_bf16.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i, _i, _p, _p, _p]
     L.orc_combine_bf16.restype = None
-    L.orc_combine_token_fp8.argtypes = [_i, _i, _i, _i, _p, _p, _p, _p, _p, _p]
+    L.orc_combine_token_fp8.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _p, _p, _p, _p]
     L.orc_combine_token_fp8.restype = None
-    L.orc_combine_fp8.argtypes = [_i, _i, _i, _i, _i, _p, _p, _p, _i, _i, _p, _p, _p, _p,
-                                  _p, _p, _p]
+    L.orc_combine_fp8.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i, _i, _p, _p, _p,
+                                  _p, _p, _p, _p]
     L.orc_combine_fp8.restype = None
     L.orc_allgatherv.argtypes = [_i, _p, _i64, _p, _i64, _p]
     L.orc_allgatherv.restype = None
@@ -145,8 +145,12 @@ def fp8_quantize_row(x_bits: np.ndarray):
 # dispatch / combine
 # --------------------------------------------------------------------------
 
+def _active(active, P):
+    return (1 << P) - 1 if active is None else int(active)
+
+
 def dispatch(counts, payload, ids, weights=None, scales=None, *, E: int,
-             invalid_id=None, r0: int = 0, r1=None, want_payload: bool = True):
+             invalid_id=None, r0: int = 0, r1=None, want_payload: bool = True, active=None):
     """Receive planes of destinations r0..r1-1.
 
     payload: uint8 [P, T, row_bytes]; scales: uint8 [P, T, srow] or None;
@@ -172,26 +176,27 @@ def dispatch(counts, payload, ids, weights=None, scales=None, *, E: int,
         "scales": np.zeros((nr, P * T, srow), np.uint8) if (srow and want_payload) else None,
         "weights": np.zeros((nr, P * T, k), np.float32) if weights is not None else None,
     }
-    lib().orc_dispatch(P, T, k, E, inv, _ptr(counts), _ptr(payload), row, _ptr(scales), srow,
+    lib().orc_dispatch(P, T, k, E, inv, _active(active, P), _ptr(counts), _ptr(payload), row,
+                       _ptr(scales), srow,
                        _ptr(ids), _ptr(weights), r0, r1, _ptr(out["payload"]),
                        _ptr(out["scales"]), _ptr(out["ids"]), _ptr(out["weights"]),
                        _ptr(out["valid"]), _ptr(out["counts"]), _ptr(out["slots"]))
     return out
 
 
-def combine_token_bf16(ids_row, eo_rows, *, E: int):
+def combine_token_bf16(ids_row, eo_rows, *, E: int, active=None):
     """One token: eo_rows uint16 [P, H] (its slot's row on every rank)."""
     ids_row = _c(ids_row, np.int32)
     eo_rows = _c(eo_rows, np.uint16)
     P, H = eo_rows.shape
     ref = np.zeros(H, np.float64)
     y = np.zeros(H, np.uint16)
-    lib().orc_combine_token_bf16(P, H, ids_row.shape[0], E, _ptr(ids_row), _ptr(eo_rows),
-                                 _ptr(ref), _ptr(y))
+    lib().orc_combine_token_bf16(P, H, ids_row.shape[0], E, _active(active, P), _ptr(ids_row),
+                                 _ptr(eo_rows), _ptr(ref), _ptr(y))
     return ref, y
 
 
-def combine_bf16(counts, ids, eo, *, E: int, s0: int = 0, s1=None):
+def combine_bf16(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None):
     """BF16 combine of source ranks s0..s1-1; eo uint16 [P, P*T, H].
     Returns (ref float64 [n, T, H], y uint16 [n, T, H]); rows t >= n_s
     stay zero."""
@@ -204,12 +209,12 @@ def combine_bf16(counts, ids, eo, *, E: int, s0: int = 0, s1=None):
     ref = np.zeros((s1 - s0, T, H), np.float64)
     y = np.zeros((s1 - s0, T, H), np.uint16)
     scratch = np.zeros((P, H), np.uint16)
-    lib().orc_combine_bf16(P, T, H, k, E, _ptr(counts), _ptr(ids), _ptr(eo), s0, s1,
-                           _ptr(ref), _ptr(y), _ptr(scratch))
+    lib().orc_combine_bf16(P, T, H, k, E, _active(active, P), _ptr(counts), _ptr(ids), _ptr(eo),
+                           s0, s1, _ptr(ref), _ptr(y), _ptr(scratch))
     return ref, y
 
 
-def combine_token_fp8(ids_row, eo_rows, *, E: int):
+def combine_token_fp8(ids_row, eo_rows, *, E: int, active=None):
     ids_row = _c(ids_row, np.int32)
     eo_rows = _c(eo_rows, np.uint16)
     P, H = eo_rows.shape
@@ -217,12 +222,12 @@ def combine_token_fp8(ids_row, eo_rows, *, E: int):
     scales = np.zeros((P, H // 32), np.uint8)
     ref = np.zeros(H, np.float64)
     y = np.zeros(H, np.uint16)
-    lib().orc_combine_token_fp8(P, H, ids_row.shape[0], E, _ptr(ids_row), _ptr(eo_rows),
-                                _ptr(codes), _ptr(scales), _ptr(ref), _ptr(y))
+    lib().orc_combine_token_fp8(P, H, ids_row.shape[0], E, _active(active, P), _ptr(ids_row),
+                                _ptr(eo_rows), _ptr(codes), _ptr(scales), _ptr(ref), _ptr(y))
     return codes, scales, ref, y
 
 
-def combine_fp8(counts, ids, eo, *, E: int, s0: int = 0, s1=None):
+def combine_fp8(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None):
     """FP8 combine of source ranks s0..s1-1.  Returns (land_codes
     [n, P*T, H], land_scales [n, P*T, H/32], ref_q [n, T, H] float64,
     y [n, T, H] uint16)."""
@@ -240,9 +245,9 @@ def combine_fp8(counts, ids, eo, *, E: int, s0: int = 0, s1=None):
     sr = np.zeros((P, H), np.uint16)
     sc = np.zeros((P, H), np.uint8)
     ss = np.zeros((P, H // 32), np.uint8)
-    lib().orc_combine_fp8(P, T, H, k, E, _ptr(counts), _ptr(ids), _ptr(eo), s0, s1,
-                          _ptr(land_codes), _ptr(land_scales), _ptr(ref), _ptr(y), _ptr(sr),
-                          _ptr(sc), _ptr(ss))
+    lib().orc_combine_fp8(P, T, H, k, E, _active(active, P), _ptr(counts), _ptr(ids), _ptr(eo),
+                          s0, s1, _ptr(land_codes), _ptr(land_scales), _ptr(ref), _ptr(y),
+                          _ptr(sr), _ptr(sc), _ptr(ss))
     return land_codes, land_scales, ref, y
 
 

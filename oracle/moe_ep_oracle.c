@@ -40,6 +40,11 @@
  *  - every slot that receives no row carries invalid_id in all k id
  *    entries, not only the slots past a source's token count;
  *  - output rounding is round-to-nearest-even to bf16;
+ *  - active rank mask (FlashInfer "flashinfer.comm.moe_a2a_dispatch",
+ *    active_rank_mask parameter: tokens routed to a masked-off rank are
+ *    dropped): with every virtual rank in one call, a masked-off rank
+ *    neither sends nor receives; nothing is written into its receive
+ *    planes and combine produces no rows for it;
  *  - the FP8 combine payload is OCP e4m3fn with one power-of-two (e8m0)
  *    scale per 32 elements, the scale being the smallest power of two
  *    that keeps the block's largest magnitude within 448.
@@ -200,6 +205,12 @@ int orc_token_goes_to(const int32_t *ids_row, int k, int E, int P, int r)
     return 0;
 }
 
+/* 1 when rank r takes part in the step (bit r of the active mask). */
+static int live(uint64_t active, int r)
+{
+    return (int)((active >> r) & 1u);
+}
+
 /* ------------------------------------------------------------------ */
 /* dispatch                                                            */
 /* ------------------------------------------------------------------ */
@@ -220,9 +231,11 @@ int orc_token_goes_to(const int32_t *ids_row, int k, int E, int P, int r)
  * recv_weights [.][P*T][k], recv_valid [.][P*T] (1/0),
  * recv_counts [.][P] (rows received from each source),
  * recv_slots [.][P*T] (valid slots in ascending order, then -1).
- * Any output pointer except recv_ids may be NULL.
+ * Any output pointer except recv_ids may be NULL.  Ranks whose bit in
+ * active is clear neither send nor receive: their outputs are left
+ * untouched, and their tokens reach no rank.
  */
-void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id,
+void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id, uint64_t active,
                   const int32_t *counts,
                   const uint8_t *payload, int64_t row_bytes,
                   const uint8_t *scales, int64_t srow_bytes,
@@ -237,12 +250,14 @@ void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id,
     for (int r = r0; r < r1; ++r) {
         int64_t ro = r - r0;
         int64_t nslot = 0;
+        if (!live(active, r))
+            continue;
         for (int s = 0; s < P; ++s) {
             int32_t from_s = 0;
             for (int t = 0; t < T; ++t) {
                 int64_t q = (int64_t)s * T + t;
                 const int32_t *id_row = ids + ((int64_t)s * T + t) * k;
-                int valid = t < counts[s] && orc_token_goes_to(id_row, k, E, P, r);
+                int valid = live(active, s) && t < counts[s] && orc_token_goes_to(id_row, k, E, P, r);
                 int32_t *out_ids = recv_ids + (ro * slots + q) * k;
                 if (recv_valid)
                     recv_valid[ro * slots + q] = (uint8_t)valid;
@@ -286,15 +301,15 @@ void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id,
  * (whatever it holds where the token was not sent).  ref[H] is the exact
  * sum (double) over ranks r that own one of the token's experts, in
  * ascending r; y[H] is ref rounded to bf16.  A token sent nowhere gives
- * +0.
+ * +0.  Ranks whose bit in active is clear contribute nothing.
  */
-void orc_combine_token_bf16(int P, int H, int k, int E, const int32_t *ids_row,
+void orc_combine_token_bf16(int P, int H, int k, int E, uint64_t active, const int32_t *ids_row,
                             const uint16_t *eo_rows, double *ref, uint16_t *y)
 {
     for (int h = 0; h < H; ++h)
         ref[h] = 0.0;
     for (int r = 0; r < P; ++r) {
-        if (!orc_token_goes_to(ids_row, k, E, P, r))
+        if (!live(active, r) || !orc_token_goes_to(ids_row, k, E, P, r))
             continue;
         for (int h = 0; h < H; ++h)
             ref[h] += orc_bf16_to_double(eo_rows[(int64_t)r * H + h]);
@@ -306,21 +321,22 @@ void orc_combine_token_bf16(int P, int H, int k, int E, const int32_t *ids_row,
 /*
  * BF16 combine for source ranks s in [s0, s1): eo [P][P*T][H] is every
  * rank's expert output by slot, ref / y are [s1-s0][T][H]; rows t >= n_s
- * are left untouched (the result holds local_num_tokens rows).
+ * are left untouched (the result holds local_num_tokens rows), and so are
+ * all rows of a source whose bit in active is clear.
  */
-void orc_combine_bf16(int P, int T, int H, int k, int E, const int32_t *counts,
+void orc_combine_bf16(int P, int T, int H, int k, int E, uint64_t active, const int32_t *counts,
                       const int32_t *ids, const uint16_t *eo, int s0, int s1,
                       double *ref, uint16_t *y, uint16_t *scratch_rows /* [P][H] */)
 {
     int64_t slots = (int64_t)P * T;
     for (int s = s0; s < s1; ++s)
-        for (int t = 0; t < counts[s]; ++t) {
+        for (int t = 0; live(active, s) && t < counts[s]; ++t) {
             int64_t q = (int64_t)s * T + t;
             for (int r = 0; r < P; ++r)
                 memcpy(scratch_rows + (int64_t)r * H, eo + ((int64_t)r * slots + q) * H,
                        sizeof(uint16_t) * (size_t)H);
             int64_t o = ((int64_t)(s - s0) * T + t) * H;
-            orc_combine_token_bf16(P, H, k, E, ids + q * k, scratch_rows, ref + o, y + o);
+            orc_combine_token_bf16(P, H, k, E, active, ids + q * k, scratch_rows, ref + o, y + o);
         }
 }
 
@@ -331,14 +347,14 @@ void orc_combine_bf16(int P, int T, int H, int k, int E, const int32_t *counts,
  * Rows of ranks the token was not sent to are left untouched in codes /
  * scales.
  */
-void orc_combine_token_fp8(int P, int H, int k, int E, const int32_t *ids_row,
+void orc_combine_token_fp8(int P, int H, int k, int E, uint64_t active, const int32_t *ids_row,
                            const uint16_t *eo_rows, uint8_t *codes, uint8_t *scales,
                            double *ref_q, uint16_t *y)
 {
     for (int h = 0; h < H; ++h)
         ref_q[h] = 0.0;
     for (int r = 0; r < P; ++r) {
-        if (!orc_token_goes_to(ids_row, k, E, P, r))
+        if (!live(active, r) || !orc_token_goes_to(ids_row, k, E, P, r))
             continue;
         uint8_t *c = codes + (int64_t)r * H;
         uint8_t *sc = scales + (int64_t)r * (H / 32);
@@ -357,7 +373,7 @@ void orc_combine_token_fp8(int P, int H, int k, int E, const int32_t *ids_row,
  * land_scales [s1-s0][P*T][H/32] (slots with no row are untouched).
  * ref_q / y are [s1-s0][T][H].
  */
-void orc_combine_fp8(int P, int T, int H, int k, int E, const int32_t *counts,
+void orc_combine_fp8(int P, int T, int H, int k, int E, uint64_t active, const int32_t *counts,
                      const int32_t *ids, const uint16_t *eo, int s0, int s1,
                      uint8_t *land_codes, uint8_t *land_scales, double *ref_q, uint16_t *y,
                      uint16_t *scratch_rows /* [P][H] */,
@@ -365,16 +381,16 @@ void orc_combine_fp8(int P, int T, int H, int k, int E, const int32_t *counts,
 {
     int64_t slots = (int64_t)P * T;
     for (int s = s0; s < s1; ++s)
-        for (int t = 0; t < counts[s]; ++t) {
+        for (int t = 0; live(active, s) && t < counts[s]; ++t) {
             int64_t q = (int64_t)s * T + t;
             for (int r = 0; r < P; ++r)
                 memcpy(scratch_rows + (int64_t)r * H, eo + ((int64_t)r * slots + q) * H,
                        sizeof(uint16_t) * (size_t)H);
             int64_t o = ((int64_t)(s - s0) * T + t) * H;
-            orc_combine_token_fp8(P, H, k, E, ids + q * k, scratch_rows, scratch_codes,
+            orc_combine_token_fp8(P, H, k, E, active, ids + q * k, scratch_rows, scratch_codes,
                                   scratch_scales, ref_q + o, y + o);
             for (int r = 0; r < P; ++r) {
-                if (!orc_token_goes_to(ids + q * k, k, E, P, r))
+                if (!live(active, r) || !orc_token_goes_to(ids + q * k, k, E, P, r))
                     continue;
                 int64_t land = (int64_t)(s - s0) * slots + (int64_t)r * T + t;
                 memcpy(land_codes + land * H, scratch_codes + (int64_t)r * H, (size_t)H);

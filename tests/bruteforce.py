@@ -18,15 +18,20 @@ def _bf16_bits_to_float(bits):
     return torch.from_numpy(np.asarray(bits, np.uint16).view(np.int16)).view(torch.bfloat16).double().numpy()
 
 
-def dispatch(counts, payload, ids, weights, scales, E):
+def dispatch(counts, payload, ids, weights, scales, E, alive=None):
+    """alive: set of ranks taking part (all when None); others neither
+    send nor receive (FlashInfer moe_a2a_dispatch, active_rank_mask)."""
     P, T, k = ids.shape
     epr = E // P
+    alive = set(range(P)) if alive is None else set(alive)
     recv = [dict() for _ in range(P)]
     for s in range(P):
+        if s not in alive:
+            continue
         for t in range(int(counts[s])):
             dests = set()
             for e in ids[s][t]:
-                if 0 <= int(e) < E:
+                if 0 <= int(e) < E and int(e) // epr in alive:
                     dests.add(int(e) // epr)
             for r in dests:
                 recv[r][s * T + t] = (
@@ -56,15 +61,18 @@ def counts_and_slots(recv, P, T):
     return cnt, slots
 
 
-def combine_bf16(counts, ids, eo_bits, E):
+def combine_bf16(counts, ids, eo_bits, E, alive=None):
     """Sum, per source token, the rows its destinations hold in its slot.
     Returns {(s, t): list of float sums} (Python floats, ascending r)."""
     P, T, k = ids.shape
     epr = E // P
+    alive = set(range(P)) if alive is None else set(alive)
     out = {}
     for s in range(P):
+        if s not in alive:
+            continue
         for t in range(int(counts[s])):
-            dests = sorted({int(e) // epr for e in ids[s][t] if 0 <= int(e) < E})
+            dests = sorted({int(e) // epr for e in ids[s][t] if 0 <= int(e) < E} & alive)
             acc = [0.0] * eo_bits.shape[-1]
             for r in dests:
                 row = _bf16_bits_to_float(eo_bits[r, s * T + t])
