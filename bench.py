@@ -178,7 +178,7 @@ class Setup:
         self._args = (C.c_void_p(self.payload.data_ptr()),
                       C.c_void_p(self.scales.data_ptr()) if self.scales is not None else None,
                       C.c_void_p(self.ids.data_ptr()), C.c_void_p(self.weights.data_ptr()),
-                      (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T))
+                      (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T), None)
         self._eo = C.c_void_p(self.eo.data_ptr())
         self._out = C.c_void_p(self.out.data_ptr())
 

@@ -218,7 +218,7 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
 int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
                     const int32_t *topk_ids, const float *topk_weights,
                     const int32_t *num_tokens, int32_t runtime_max_tokens_per_rank,
-                    void *stream, moe_ep_dispatch_views *views)
+                    const uint64_t *active_rank_mask, void *stream, moe_ep_dispatch_views *views)
 {
     if (!live_handle(h))
         return fail(MOE_EP_ERR_INVALID_ARG, "invalid or destroyed handle");
@@ -248,6 +248,10 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
         if (num_tokens[s] < 0 || num_tokens[s] > T)
             return fail(MOE_EP_ERR_INVALID_ARG,
                         "num_tokens[" + std::to_string(s) + "] must be in [0, T]");
+    const uint64_t all = p.ep_size == 64 ? ~0ull : ((1ull << p.ep_size) - 1);
+    const uint64_t active = active_rank_mask ? *active_rank_mask : all;
+    if (active & ~all)
+        return fail(MOE_EP_ERR_INVALID_ARG, "active_rank_mask has bits set at or above ep_size");
 
     DispatchArgs a;
     std::memset(&a, 0, sizeof a);
@@ -277,8 +281,9 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
         if ((1 << sh) == a.epr)
             a.epr_shift = sh;
     a.invalid_id = p.invalid_expert_id;
+    a.active = active;
     for (int s = 0; s < p.ep_size; ++s)
-        a.n[s] = num_tokens[s];
+        a.n[s] = ((active >> s) & 1u) ? num_tokens[s] : 0; // masked-off ranks send nothing
 
     hipError_t e = launch_dispatch(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
@@ -286,7 +291,7 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
     h->dispatched = true;
     h->T = T;
     for (int s = 0; s < p.ep_size; ++s)
-        h->n[s] = num_tokens[s];
+        h->n[s] = a.n[s];
     if (views) {
         views->tokens_per_rank = T;
         views->ep_size = p.ep_size;

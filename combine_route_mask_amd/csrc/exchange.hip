@@ -88,8 +88,8 @@ __device__ __forceinline__ uint64_t owner_bit(const DispatchArgs &a, int id)
 }
 
 // Destination-rank mask of token q: bit r set when one of its k ids is an
-// expert of rank r.  OR-ing the bits deduplicates tokens with several
-// experts on one rank.  KQ > 0: the k = 4*KQ ids are read as KQ 16-byte
+// expert of rank r and rank r takes part in the step.  OR-ing the bits
+// deduplicates tokens with several experts on one rank.  KQ > 0: the k = 4*KQ ids are read as KQ 16-byte
 // vectors; KQ == 0: any k, all loads of the first 16 ids issued together.
 template <int KQ>
 __device__ __forceinline__ uint64_t route_mask(const DispatchArgs &a, int64_t q)
@@ -118,7 +118,7 @@ __device__ __forceinline__ uint64_t route_mask(const DispatchArgs &a, int64_t q)
         for (int j = 0; j < a.k; ++j)
             m |= owner_bit(a, idrow[j]);
     }
-    return m;
+    return m & a.active; // masked-off ranks receive nothing
 }
 
 // Count of set bits of 'bits' in lanes below this one (v_mbcnt).
@@ -172,6 +172,8 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
 {
     __shared__ int wave_tot[kScanUnroll][kWaves];
     __shared__ int src_off[MOE_EP_MAX_RANKS + 1];
+    if (!((a.active >> r) & 1u)) // a masked-off rank's region is left alone
+        return;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint8_t *region = a.ws + (int64_t)r * a.region;
     int32_t *slots = reinterpret_cast<int32_t *>(region + a.off_slots);
@@ -268,8 +270,8 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
 // store every token's mask in its source rank's region, for combine).  Then
 // the block walks the chunk's id rows in 16-byte units (KQ > 0) or words,
 // each unit read once (only for tokens that go somewhere) and stored to
-// every destination of the group: a slot whose token goes to r gets the
-// token's ids and weights, every other slot k copies of invalid_id.
+// every live destination of the group: a slot whose token goes to r gets
+// the token's ids and weights, every other slot k copies of invalid_id.
 // Consecutive lanes write consecutive units.
 template <int KQ>
 __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c)
@@ -284,7 +286,7 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
         const int t = (int)(q - (int64_t)s * a.T);
         const uint64_t mask = t < a.n[s] ? route_mask<KQ>(a, q) : 0ull;
         smask[threadIdx.x] = mask;
-        if (r0 == 0)
+        if (r0 == 0 && ((a.active >> s) & 1u))
             *reinterpret_cast<uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks +
                                           (int64_t)t * 8) = mask;
     }
@@ -301,6 +303,8 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
             const u32x4 idv = mk ? ids_in[e] : marker;
             const u32x4 wv = (mk && w_in) ? w_in[e] : marker;
             for (int r = r0; r < r1; ++r) {
+                if (!((a.active >> r) & 1u))
+                    continue;
                 uint8_t *reg = a.ws + (int64_t)r * a.region;
                 const bool go = (mk >> r) & 1u;
                 reinterpret_cast<u32x4 *>(reg + a.off_ids)[q0 * KQ + e] = go ? idv : marker;
@@ -317,6 +321,8 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
             const int32_t idv = mk ? ids_in[e] : a.invalid_id;
             const float wv = (mk && w_in) ? w_in[e] : 0.0f;
             for (int r = r0; r < r1; ++r) {
+                if (!((a.active >> r) & 1u))
+                    continue;
                 uint8_t *reg = a.ws + (int64_t)r * a.region;
                 const bool go = (mk >> r) & 1u;
                 reinterpret_cast<int32_t *>(reg + a.off_ids)[q0 * a.k + e] = go ? idv : a.invalid_id;

@@ -34,7 +34,8 @@ struct DispatchArgs {
     int64_t row_bytes, srow_bytes;
     int32_t P, T, k, E, epr, invalid_id;
     int32_t epr_shift;               // log2(epr) when epr is a power of two, else -1
-    int32_t n[MOE_EP_MAX_RANKS];     // local token counts
+    uint64_t active;                 // bit r: rank r takes part in the step
+    int32_t n[MOE_EP_MAX_RANKS];     // local token counts (0 for masked-off ranks)
 };
 
 struct CombineArgs {

@@ -84,8 +84,8 @@ def _load(path: str = LIB_PATH):
     L.moe_ep_workspace_bytes.restype = C.c_size_t
     L.moe_ep_create.argtypes = [C.POINTER(Params), vp, C.c_size_t, C.POINTER(vp)]
     L.moe_ep_create.restype = C.c_int
-    L.moe_ep_dispatch.argtypes = [vp, vp, vp, vp, vp, C.POINTER(i32), i32, vp,
-                                  C.POINTER(DispatchViews)]
+    L.moe_ep_dispatch.argtypes = [vp, vp, vp, vp, vp, C.POINTER(i32), i32,
+                                  C.POINTER(C.c_uint64), vp, C.POINTER(DispatchViews)]
     L.moe_ep_dispatch.restype = C.c_int
     L.moe_ep_combine.argtypes = [vp, vp, vp, vp]
     L.moe_ep_combine.restype = C.c_int
@@ -161,11 +161,13 @@ def moe_ep_create(params: Params, workspace_ptr: int, size_per_rank: int) -> C.c
 
 
 def moe_ep_dispatch(handle, hidden, scales, topk_ids, topk_weights, num_tokens,
-                    runtime_max_tokens_per_rank: int = 0, stream=None) -> DispatchViews:
+                    runtime_max_tokens_per_rank: int = 0, stream=None,
+                    active_rank_mask: Optional[int] = None) -> DispatchViews:
     counts, cptr = _i32_array(num_tokens)
     views = DispatchViews()
+    mask = None if active_rank_mask is None else C.byref(C.c_uint64(int(active_rank_mask)))
     _check(lib.moe_ep_dispatch(handle, _ptr(hidden), _ptr(scales), _ptr(topk_ids),
-                               _ptr(topk_weights), cptr, int(runtime_max_tokens_per_rank),
+                               _ptr(topk_weights), cptr, int(runtime_max_tokens_per_rank), mask,
                                _stream(stream), C.byref(views)))
     del counts
     return views
@@ -260,7 +262,8 @@ class MoeEpExchange:
         return v if dtype is None else v.view(dtype)
 
     def dispatch(self, hidden, topk_ids, topk_weights=None, scales=None, num_tokens=None,
-                 runtime_max_tokens_per_rank: Optional[int] = None, stream=None):
+                 runtime_max_tokens_per_rank: Optional[int] = None, stream=None,
+                 active_rank_mask: Optional[int] = None):
         import torch
         P = self.P
         T = runtime_max_tokens_per_rank or self.params.max_tokens_per_rank
@@ -287,7 +290,7 @@ class MoeEpExchange:
             num_tokens = [T] * P
         _need(len(num_tokens) == P, "num_tokens needs one entry per rank")
         v = moe_ep_dispatch(self.handle, hidden, scales, topk_ids, topk_weights, num_tokens,
-                            T, stream)
+                            T, stream, active_rank_mask)
         self.views = v
         k = self.params.top_k
         out = {

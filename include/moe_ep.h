@@ -147,6 +147,12 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
  *  num_tokens        host [P]: local_num_tokens n_s, 0 <= n_s <= T
  *  runtime_max_tokens_per_rank  T (the step's tokens_per_rank); <= 0
  *                    means the capacity; T <= capacity
+ *  active_rank_mask  host, one word (NULL = every rank): bit r set when
+ *                    rank r takes part in the step (moe_a2a_dispatch,
+ *                    active_rank_mask).  A masked-off rank neither sends
+ *                    nor receives: tokens routed to it are dropped, nothing
+ *                    is written into its region, and the following combine
+ *                    produces no rows for it.  Bits >= P must be clear.
  *  views             out (may be NULL): where the receive planes are
  * Rows t >= n_s of the inputs are never read.  Writes, for every rank r and
  * slot q = s*T + t: the token's payload row, scale row, k ids and k weights
@@ -157,10 +163,12 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
 int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
                     const int32_t *topk_ids, const float *topk_weights,
                     const int32_t *num_tokens, int32_t runtime_max_tokens_per_rank,
-                    void *stream, moe_ep_dispatch_views *views);
+                    const uint64_t *active_rank_mask, void *stream,
+                    moe_ep_dispatch_views *views);
 
 /*
- * Combine (NVLinkTwoSidedAlltoAll.combine) of the last dispatch.
+ * Combine (NVLinkTwoSidedAlltoAll.combine) of the last dispatch (and of
+ * its active rank mask).
  *  expert_output  device [P][P*T][H] bf16: rank r's row for slot q at
  *                 (r*P*T + q)*H; only slots that received a token are read
  *  output         device [P][T][H] bf16: row t of rank s receives the sum

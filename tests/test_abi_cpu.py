@@ -97,11 +97,11 @@ def test_create_checks_workspace_before_device(m):
 def test_calls_on_bad_handles(m):
     counts = (C.c_int32 * 8)(*([1] * 8))
     assert m.lib.moe_ep_dispatch(None, C.c_void_p(256), None, C.c_void_p(256), None, counts, 0,
-                                 None, None) == m.ERR_INVALID_ARG
+                                 None, None, None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_combine(None, C.c_void_p(256), C.c_void_p(256), None) == m.ERR_INVALID_ARG
     bogus = C.c_void_p(0x1234560)
     assert m.lib.moe_ep_dispatch(bogus, C.c_void_p(256), None, C.c_void_p(256), None, counts, 0,
-                                 None, None) == m.ERR_INVALID_ARG
+                                 None, None, None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_destroy(None) == 0
     assert m.lib.moe_ep_destroy(bogus) == 0  # unknown handles are ignored
 
