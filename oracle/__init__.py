@@ -72,8 +72,8 @@ def _declare(L):
     L.orc_owner.restype = _i
     L.orc_token_goes_to.argtypes = [_p, _i, _i, _i, _i]
     L.orc_token_goes_to.restype = _i
-    L.orc_dispatch.argtypes = [_i, _i, _i, _i, C.c_int32, C.c_uint64, _p, _p, _i64, _p, _i64, _p,
-                               _p, _i, _i, _p, _p, _p, _p, _p, _p, _p]
+    L.orc_dispatch.argtypes = [_i, _i, _i, _i, C.c_int32, C.c_uint64, _p, _p, _i64, _p, _i64,
+                               _p, _i64, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
     L.orc_dispatch.restype = None
     L.orc_combine_token_bf16.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _p, _p]
     L.orc_combine_token_bf16.restype = None
@@ -84,6 +84,8 @@ def _declare(L):
     L.orc_combine_fp8.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i, _i, _p, _p, _p,
                                   _p, _p, _p, _p]
     L.orc_combine_fp8.restype = None
+    L.orc_eplb_allgather.argtypes = [_i, _i, C.c_uint64, _p, _i, _p]
+    L.orc_eplb_allgather.restype = None
     L.orc_allgatherv.argtypes = [_i, _p, _i64, _p, _i64, _p]
     L.orc_allgatherv.restype = None
     L.orc_reduce_scatterv.argtypes = [_i, _p, _i, _p, _i, _p, _p]
@@ -150,7 +152,8 @@ def _active(active, P):
 
 
 def dispatch(counts, payload, ids, weights=None, scales=None, *, E: int,
-             invalid_id=None, r0: int = 0, r1=None, want_payload: bool = True, active=None):
+             invalid_id=None, r0: int = 0, r1=None, want_payload: bool = True, active=None,
+             extra=None):
     """Receive planes of destinations r0..r1-1.
 
     payload: uint8 [P, T, row_bytes]; scales: uint8 [P, T, srow] or None;
@@ -164,6 +167,8 @@ def dispatch(counts, payload, ids, weights=None, scales=None, *, E: int,
     scales = _c(scales, np.uint8)
     srow = 0 if scales is None else scales.shape[-1]
     weights = _c(weights, np.float32)
+    extra = _c(extra, np.uint8)
+    xrow = 0 if extra is None else extra.shape[-1]
     r1 = P if r1 is None else r1
     nr = r1 - r0
     inv = E if invalid_id is None else invalid_id
@@ -174,13 +179,25 @@ def dispatch(counts, payload, ids, weights=None, scales=None, *, E: int,
         "slots": np.zeros((nr, P * T), np.int32),
         "payload": np.zeros((nr, P * T, row), np.uint8) if want_payload else None,
         "scales": np.zeros((nr, P * T, srow), np.uint8) if (srow and want_payload) else None,
+        "extra": np.zeros((nr, P * T, xrow), np.uint8) if (xrow and want_payload) else None,
         "weights": np.zeros((nr, P * T, k), np.float32) if weights is not None else None,
     }
     lib().orc_dispatch(P, T, k, E, inv, _active(active, P), _ptr(counts), _ptr(payload), row,
-                       _ptr(scales), srow,
+                       _ptr(scales), srow, _ptr(extra), xrow,
                        _ptr(ids), _ptr(weights), r0, r1, _ptr(out["payload"]),
-                       _ptr(out["scales"]), _ptr(out["ids"]), _ptr(out["weights"]),
-                       _ptr(out["valid"]), _ptr(out["counts"]), _ptr(out["slots"]))
+                       _ptr(out["scales"]), _ptr(out["extra"]), _ptr(out["ids"]),
+                       _ptr(out["weights"]), _ptr(out["valid"]), _ptr(out["counts"]),
+                       _ptr(out["slots"]))
+    return out
+
+
+def eplb_allgather(stats, r: int, active=None, out=None):
+    """Rank r's gathered [P, n] statistics from stats [P, n] int32 (rows of
+    masked-off ranks keep out's previous contents)."""
+    stats = _c(stats, np.int32)
+    P, n = stats.shape
+    out = np.zeros((P, n), np.int32) if out is None else np.ascontiguousarray(out, np.int32)
+    lib().orc_eplb_allgather(P, n, _active(active, P), _ptr(stats), r, _ptr(out))
     return out
 
 

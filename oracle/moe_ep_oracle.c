@@ -40,6 +40,12 @@
  *  - every slot that receives no row carries invalid_id in all k id
  *    entries, not only the slots past a source's token count;
  *  - output rounding is round-to-nearest-even to bf16;
+ *  - extra per-token payload bytes (FlashInfer "NVLinkOneSidedConfig",
+ *    options paragraph, extra_payload_bytes_per_token) travel with the
+ *    token like its scale row;
+ *  - EPLB statistics (same paragraph, eplb_stats_num_experts; FlashInfer
+ *    "moe_a2a_dispatch", eplb_local_stats / eplb_gathered_stats): row r of
+ *    the gathered [ep_size, n] matrix holds rank r's statistics;
  *  - active rank mask (FlashInfer "flashinfer.comm.moe_a2a_dispatch",
  *    active_rank_mask parameter: tokens routed to a masked-off rank are
  *    dropped): with every virtual rank in one call, a masked-off rank
@@ -219,15 +225,16 @@ static int live(uint64_t active, int r)
  * Receive planes of destination ranks r in [r0, r1).
  *
  * Inputs are stacked over source ranks: payload [P][T][row_bytes],
- * scales [P][T][srow_bytes] (or NULL), ids [P][T][k], weights [P][T][k]
- * (or NULL), counts [P] (n_s <= T).  Slot q = s * T + t of destination r
+ * scales [P][T][srow_bytes] (or NULL), extra [P][T][xrow_bytes] (or
+ * NULL), ids [P][T][k], weights [P][T][k] (or NULL), counts [P] (n_s <= T).  Slot q = s * T + t of destination r
  * is valid when t < n_s and r owns one of the token's experts; it then
  * holds the token's payload bytes, scale bytes, all k ids unchanged and
  * all k weights.  Other slots hold invalid_id in every id entry; their
  * payload, scale and weight entries are not defined (left untouched).
  *
  * Outputs, indexed by (r - r0): recv_payload [.][P*T][row_bytes],
- * recv_scales [.][P*T][srow_bytes], recv_ids [.][P*T][k],
+ * recv_scales [.][P*T][srow_bytes], recv_extra [.][P*T][xrow_bytes],
+ * recv_ids [.][P*T][k],
  * recv_weights [.][P*T][k], recv_valid [.][P*T] (1/0),
  * recv_counts [.][P] (rows received from each source),
  * recv_slots [.][P*T] (valid slots in ascending order, then -1).
@@ -239,9 +246,10 @@ void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id, uint64_t activ
                   const int32_t *counts,
                   const uint8_t *payload, int64_t row_bytes,
                   const uint8_t *scales, int64_t srow_bytes,
+                  const uint8_t *extra, int64_t xrow_bytes,
                   const int32_t *ids, const float *weights,
                   int r0, int r1,
-                  uint8_t *recv_payload, uint8_t *recv_scales,
+                  uint8_t *recv_payload, uint8_t *recv_scales, uint8_t *recv_extra,
                   int32_t *recv_ids, float *recv_weights,
                   uint8_t *recv_valid, int32_t *recv_counts,
                   int32_t *recv_slots)
@@ -278,6 +286,9 @@ void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id, uint64_t activ
                 if (recv_scales && scales && srow_bytes > 0)
                     memcpy(recv_scales + (ro * slots + q) * srow_bytes,
                            scales + ((int64_t)s * T + t) * srow_bytes, (size_t)srow_bytes);
+                if (recv_extra && extra && xrow_bytes > 0)
+                    memcpy(recv_extra + (ro * slots + q) * xrow_bytes,
+                           extra + ((int64_t)s * T + t) * xrow_bytes, (size_t)xrow_bytes);
                 if (recv_weights && weights)
                     for (int j = 0; j < k; ++j)
                         recv_weights[(ro * slots + q) * k + j] = weights[((int64_t)s * T + t) * k + j];
@@ -288,6 +299,24 @@ void orc_dispatch(int P, int T, int k, int E, int32_t invalid_id, uint64_t activ
         if (recv_slots)
             for (int64_t i = nslot; i < slots; ++i)
                 recv_slots[ro * slots + i] = -1;
+    }
+}
+
+/*
+ * EPLB statistics all-gathered during dispatch, as seen by rank r:
+ * out [P][n] receives row s = stats [P][n] row s for every rank s taking
+ * part; rows of masked-off ranks, and all of out when r itself is masked
+ * off, are left untouched.
+ */
+void orc_eplb_allgather(int P, int n, uint64_t active, const int32_t *stats, int r, int32_t *out)
+{
+    if (!live(active, r))
+        return;
+    for (int s = 0; s < P; ++s) {
+        if (!live(active, s))
+            continue;
+        for (int i = 0; i < n; ++i)
+            out[(int64_t)s * n + i] = stats[(int64_t)s * n + i];
     }
 }
 

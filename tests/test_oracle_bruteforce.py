@@ -104,3 +104,35 @@ def test_combine_token_agrees_with_array_form():
             assert np.array_equal(r1, ref[s, t]) and np.array_equal(y1, y[s, t])
     ref2, y2 = oracle.combine_bf16(counts, ids, eo, E=E, s0=2, s1=4)
     assert np.array_equal(ref2, ref[2:4]) and np.array_equal(y2, y[2:4])
+
+
+@pytest.mark.parametrize("P,T,k,E", SHAPES[:4])
+def test_extra_payload_travels_with_token(P, T, k, E):
+    rng = np.random.default_rng(55 + P)
+    counts, payload, ids, weights, scales = _case(rng, P, T, k, E, srow=4)
+    extra = rng.integers(0, 256, size=(P, T, 12)).astype(np.uint8)
+    got = oracle.dispatch(counts, payload, ids, weights, scales, E=E, extra=extra)
+    # the extra plane is one more per-token row: brute force it as the payload
+    recv = bf.dispatch(counts, extra, ids, weights, scales, E)
+    for r in range(P):
+        assert set(np.nonzero(got["valid"][r])[0]) == set(recv[r])
+        for q, (xb, _, _, _) in recv[r].items():
+            assert bytes(got["extra"][r, q]) == xb
+
+
+def test_eplb_allgather_is_the_stacked_rows():
+    rng = np.random.default_rng(66)
+    P, n = 5, 7
+    stats = rng.integers(-1000, 1000, size=(P, n)).astype(np.int32)
+    for r in range(P):
+        assert np.array_equal(oracle.eplb_allgather(stats, r), stats)  # row s = rank s's stats
+    alive = [0, 2, 3]
+    act = sum(1 << a for a in alive)
+    poison = np.full((P, n), -7, np.int32)
+    for r in range(P):
+        got = oracle.eplb_allgather(stats, r, active=act, out=poison.copy())
+        if r not in alive:
+            assert np.all(got == -7)
+        else:
+            for s in range(P):
+                assert np.array_equal(got[s], stats[s] if s in alive else poison[s])
