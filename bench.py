@@ -177,6 +177,7 @@ class Setup:
         self._h = self.ex.handle
         self._args = (C.c_void_p(self.payload.data_ptr()),
                       C.c_void_p(self.scales.data_ptr()) if self.scales is not None else None,
+                      None, None,
                       C.c_void_p(self.ids.data_ptr()), C.c_void_p(self.weights.data_ptr()),
                       (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T), None)
         self._eo = C.c_void_p(self.eo.data_ptr())

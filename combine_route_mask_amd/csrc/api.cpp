@@ -54,6 +54,7 @@ int64_t payload_row_bytes(const moe_ep_params &p)
     case MOE_EP_FMT_BF16: return 2 * (int64_t)p.hidden_size;
     case MOE_EP_FMT_MXFP8: return p.hidden_size;
     case MOE_EP_FMT_NVFP4: return p.hidden_size / 2;
+    case MOE_EP_FMT_DEEPSEEK_FP8: return p.hidden_size;
     default: return -1;
     }
 }
@@ -64,6 +65,7 @@ int64_t scale_row_bytes(const moe_ep_params &p)
     case MOE_EP_FMT_BF16: return 0;
     case MOE_EP_FMT_MXFP8: return p.hidden_size / 32;
     case MOE_EP_FMT_NVFP4: return p.hidden_size / 16;
+    case MOE_EP_FMT_DEEPSEEK_FP8: return (p.hidden_size / 128) * 4;
     default: return -1;
     }
 }
@@ -101,6 +103,12 @@ int check_params(const moe_ep_params *pp, Layout *lay)
     if (p.dispatch_format != MOE_EP_FMT_BF16 && p.hidden_size % 32 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG,
                     "MXFP8 / NVFP4 payloads need hidden_size % 32 == 0 (16-byte rows, whole scale blocks)");
+    if (p.dispatch_format == MOE_EP_FMT_DEEPSEEK_FP8 && p.hidden_size % 128 != 0)
+        return fail(MOE_EP_ERR_INVALID_ARG, "DeepSeekFp8 payloads need hidden_size % 128 == 0");
+    if (p.extra_payload_bytes_per_token < 0)
+        return fail(MOE_EP_ERR_INVALID_ARG, "extra_payload_bytes_per_token must be non-negative");
+    if (p.eplb_stats_num_experts < 0)
+        return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_num_experts must be non-negative");
     if (p.hidden_size % 8 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG, "combine rows need hidden_size % 8 == 0");
     if (p.combine_format == MOE_EP_COMBINE_FP8 && p.hidden_size % 32 != 0)
@@ -118,14 +126,17 @@ int check_params(const moe_ep_params *pp, Layout *lay)
     };
     L.row_bytes = row;
     L.srow_bytes = srow;
+    L.xrow_bytes = p.extra_payload_bytes_per_token;
     L.payload = take(S * row);
     L.scales = take(S * srow);
+    L.extra = take(S * L.xrow_bytes);
     L.ids = take(S * k * 4);
     L.weights = take(p.has_weights ? S * k * 4 : 0);
     L.slots = take(S * 4);
     L.counts = take((int64_t)p.ep_size * 4);
     L.src_offsets = take((int64_t)(p.ep_size + 1) * 4);
     L.masks = take((int64_t)p.max_tokens_per_rank * 8);
+    L.eplb = take((int64_t)p.ep_size * p.eplb_stats_num_experts * 4);
     if (p.combine_format == MOE_EP_COMBINE_FP8) {
         L.land_codes = take(S * p.hidden_size);
         L.land_scales = take(S * (p.hidden_size / 32));
@@ -216,6 +227,7 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
 }
 
 int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
+                    const void *extra_payload, const int32_t *eplb_local_stats,
                     const int32_t *topk_ids, const float *topk_weights,
                     const int32_t *num_tokens, int32_t runtime_max_tokens_per_rank,
                     const uint64_t *active_rank_mask, void *stream, moe_ep_dispatch_views *views)
@@ -242,6 +254,13 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
         return fail(MOE_EP_ERR_INVALID_ARG, "this dispatch format needs a scale row per token");
     if (!want_scales && scales)
         return fail(MOE_EP_ERR_INVALID_ARG, "BF16 dispatch takes no scales");
+    if (extra_payload && h->lay.xrow_bytes == 0)
+        return fail(MOE_EP_ERR_INVALID_ARG,
+                    "extra_payload given but extra_payload_bytes_per_token is 0");
+    if (eplb_local_stats && p.eplb_stats_num_experts == 0)
+        return fail(MOE_EP_ERR_INVALID_ARG, "eplb_local_stats given but eplb_stats_num_experts is 0");
+    if (eplb_local_stats && !aligned(eplb_local_stats, 4))
+        return fail(MOE_EP_ERR_INVALID_ARG, "eplb_local_stats must be 4-byte aligned");
     if (!num_tokens)
         return fail(MOE_EP_ERR_INVALID_ARG, "num_tokens is NULL");
     for (int s = 0; s < p.ep_size; ++s)
@@ -257,12 +276,18 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
     std::memset(&a, 0, sizeof a);
     a.payload = static_cast<const uint8_t *>(hidden);
     a.scales = static_cast<const uint8_t *>(scales);
+    a.extra = static_cast<const uint8_t *>(extra_payload);
+    a.eplb = eplb_local_stats;
     a.ids = topk_ids;
     a.weights = p.has_weights ? topk_weights : nullptr;
     a.ws = h->ws;
     a.region = h->lay.region;
     a.off_payload = h->lay.payload;
     a.off_scales = h->lay.scales;
+    a.off_extra = h->lay.extra;
+    a.off_eplb = h->lay.eplb;
+    a.xrow_bytes = extra_payload ? h->lay.xrow_bytes : 0;
+    a.n_eplb = p.eplb_stats_num_experts;
     a.off_ids = h->lay.ids;
     a.off_weights = h->lay.weights;
     a.off_slots = h->lay.slots;
@@ -307,6 +332,10 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
         views->src_offsets_offset = h->lay.src_offsets;
         views->combine_payload_offset = h->lay.land_codes;
         views->combine_scales_offset = h->lay.land_scales;
+        views->extra_offset = h->lay.extra;
+        views->extra_row_bytes = h->lay.xrow_bytes;
+        views->eplb_offset = eplb_local_stats ? h->lay.eplb : -1;
+        views->eplb_num_experts = p.eplb_stats_num_experts;
     }
     return ok();
 }

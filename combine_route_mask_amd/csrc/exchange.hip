@@ -160,7 +160,8 @@ __device__ __forceinline__ void copy_row_any(const uint8_t *src, int64_t nbytes,
         copy_row_words<uint8_t>(src, nbytes, mask, dst0, stride);
 }
 
-// Receive bookkeeping of destination rank r: walks every source slot q in
+// Receive bookkeeping of destination rank r (and, when given, the EPLB
+// statistics all-gather into its region): walks every source slot q in
 // ascending order, 1024 slots per step (four per lane, all id rows loaded
 // before any is tested); a wave ballot marks the slots whose token goes to
 // r, v_mbcnt gives each one its rank inside the wave, and the per-wave
@@ -174,6 +175,14 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
     __shared__ int src_off[MOE_EP_MAX_RANKS + 1];
     if (!((a.active >> r) & 1u)) // a masked-off rank's region is left alone
         return;
+    if (a.eplb) {
+        // EPLB statistics all-gather: row s of rank r's [P][n] matrix is
+        // live rank s's statistics
+        int32_t *dst = reinterpret_cast<int32_t *>(a.ws + (int64_t)r * a.region + a.off_eplb);
+        for (int i = threadIdx.x; i < a.P * a.n_eplb; i += kBlock)
+            if ((a.active >> (i / a.n_eplb)) & 1u)
+                dst[i] = a.eplb[i];
+    }
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     uint8_t *region = a.ws + (int64_t)r * a.region;
     int32_t *slots = reinterpret_cast<int32_t *>(region + a.off_slots);
@@ -336,7 +345,7 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
 
 // Chunk c of token q's payload row (kDVpt 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
-// chunk 0 also carries the scale row.
+// chunk 0 also carries the scale row and the extra payload bytes.
 template <int KQ>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
@@ -373,6 +382,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
     if (c == 0 && a.srow_bytes)
         copy_row_any(a.scales + q * a.srow_bytes, a.srow_bytes, mask,
                      a.ws + a.off_scales + q * a.srow_bytes, a.region);
+    if (c == 0 && a.xrow_bytes)
+        copy_row_any(a.extra + q * a.xrow_bytes, a.xrow_bytes, mask,
+                     a.ws + a.off_extra + q * a.xrow_bytes, a.region);
 }
 
 // One launch, three block roles touching disjoint memory:

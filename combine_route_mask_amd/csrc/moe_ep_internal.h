@@ -16,23 +16,25 @@ constexpr int kMaxPlanes = 8;
 // Byte offsets of one rank's planes inside its workspace region.
 struct Layout {
     int64_t region;                  // size_per_rank
-    int64_t payload, scales, ids, weights, slots, counts, src_offsets, masks;
+    int64_t payload, scales, extra, ids, weights, slots, counts, src_offsets, masks, eplb;
     int64_t land_codes, land_scales; // FP8 combine landing plane, -1 if absent
-    int64_t row_bytes, srow_bytes;   // payload / scale row bytes
+    int64_t row_bytes, srow_bytes, xrow_bytes; // payload / scale / extra row bytes
     int64_t total;                   // bytes needed per region
 };
 
 struct DispatchArgs {
     const uint8_t *payload;          // [P][T][row_bytes]
     const uint8_t *scales;           // [P][T][srow_bytes] or null
+    const uint8_t *extra;            // [P][T][xrow_bytes] or null
+    const int32_t *eplb;             // [P][n_eplb] or null
     const int32_t *ids;              // [P][T][k]
     const float *weights;            // [P][T][k] or null
     uint8_t *ws;                     // region r at ws + r * region
     int64_t region;
-    int64_t off_payload, off_scales, off_ids, off_weights, off_slots, off_counts,
-        off_src_offsets, off_masks;
-    int64_t row_bytes, srow_bytes;
-    int32_t P, T, k, E, epr, invalid_id;
+    int64_t off_payload, off_scales, off_extra, off_ids, off_weights, off_slots, off_counts,
+        off_src_offsets, off_masks, off_eplb;
+    int64_t row_bytes, srow_bytes, xrow_bytes;
+    int32_t P, T, k, E, epr, invalid_id, n_eplb;
     int32_t epr_shift;               // log2(epr) when epr is a power of two, else -1
     uint64_t active;                 // bit r: rank r takes part in the step
     int32_t n[MOE_EP_MAX_RANKS];     // local token counts (0 for masked-off ranks)

@@ -27,11 +27,12 @@ ERR_BAD_STATE = -3
 ERR_CAPACITY = -4
 ERR_HIP = -5
 
-FMT_BF16, FMT_MXFP8, FMT_NVFP4 = 0, 1, 2
+FMT_BF16, FMT_MXFP8, FMT_NVFP4, FMT_DEEPSEEK_FP8 = 0, 1, 2, 3
 COMBINE_BF16, COMBINE_FP8 = 0, 1
 MAX_RANKS = 64
 
-_FMT_NAMES = {"bf16": FMT_BF16, "mxfp8": FMT_MXFP8, "nvfp4": FMT_NVFP4}
+_FMT_NAMES = {"bf16": FMT_BF16, "mxfp8": FMT_MXFP8, "nvfp4": FMT_NVFP4,
+              "deepseek_fp8": FMT_DEEPSEEK_FP8}
 _COMBINE_NAMES = {"bf16": COMBINE_BF16, "fp8": COMBINE_FP8}
 
 # Every symbol include/moe_ep.h declares.
@@ -54,7 +55,8 @@ class Params(C.Structure):
     _fields_ = [("ep_size", C.c_int32), ("num_experts", C.c_int32), ("top_k", C.c_int32),
                 ("max_tokens_per_rank", C.c_int32), ("hidden_size", C.c_int32),
                 ("dispatch_format", C.c_int32), ("combine_format", C.c_int32),
-                ("has_weights", C.c_int32), ("invalid_expert_id", C.c_int32)]
+                ("has_weights", C.c_int32), ("invalid_expert_id", C.c_int32),
+                ("extra_payload_bytes_per_token", C.c_int32), ("eplb_stats_num_experts", C.c_int32)]
 
 
 class DispatchViews(C.Structure):
@@ -64,7 +66,9 @@ class DispatchViews(C.Structure):
                 ("scale_row_bytes", C.c_int64), ("ids_offset", C.c_int64),
                 ("weights_offset", C.c_int64), ("slots_offset", C.c_int64),
                 ("counts_offset", C.c_int64), ("src_offsets_offset", C.c_int64),
-                ("combine_payload_offset", C.c_int64), ("combine_scales_offset", C.c_int64)]
+                ("combine_payload_offset", C.c_int64), ("combine_scales_offset", C.c_int64),
+                ("extra_offset", C.c_int64), ("extra_row_bytes", C.c_int64),
+                ("eplb_offset", C.c_int64), ("eplb_num_experts", C.c_int64)]
 
 
 class Plane(C.Structure):
@@ -84,7 +88,7 @@ def _load(path: str = LIB_PATH):
     L.moe_ep_workspace_bytes.restype = C.c_size_t
     L.moe_ep_create.argtypes = [C.POINTER(Params), vp, C.c_size_t, C.POINTER(vp)]
     L.moe_ep_create.restype = C.c_int
-    L.moe_ep_dispatch.argtypes = [vp, vp, vp, vp, vp, C.POINTER(i32), i32,
+    L.moe_ep_dispatch.argtypes = [vp, vp, vp, vp, vp, vp, vp, C.POINTER(i32), i32,
                                   C.POINTER(C.c_uint64), vp, C.POINTER(DispatchViews)]
     L.moe_ep_dispatch.restype = C.c_int
     L.moe_ep_combine.argtypes = [vp, vp, vp, vp]
@@ -134,12 +138,14 @@ def _i32_array(vals: Sequence[int]):
 
 def make_params(ep_size: int, num_experts: int, top_k: int, max_tokens_per_rank: int,
                 hidden_size: int, dispatch_format="bf16", combine_format="bf16",
-                has_weights: bool = True, invalid_expert_id: Optional[int] = None) -> Params:
+                has_weights: bool = True, invalid_expert_id: Optional[int] = None,
+                extra_payload_bytes_per_token: int = 0, eplb_stats_num_experts: int = 0) -> Params:
     df = _FMT_NAMES.get(dispatch_format, dispatch_format)
     cf = _COMBINE_NAMES.get(combine_format, combine_format)
     return Params(ep_size, num_experts, top_k, max_tokens_per_rank, hidden_size, int(df), int(cf),
                   1 if has_weights else 0,
-                  num_experts if invalid_expert_id is None else invalid_expert_id)
+                  num_experts if invalid_expert_id is None else invalid_expert_id,
+                  int(extra_payload_bytes_per_token), int(eplb_stats_num_experts))
 
 
 def moe_ep_is_supported() -> bool:
@@ -162,11 +168,13 @@ def moe_ep_create(params: Params, workspace_ptr: int, size_per_rank: int) -> C.c
 
 def moe_ep_dispatch(handle, hidden, scales, topk_ids, topk_weights, num_tokens,
                     runtime_max_tokens_per_rank: int = 0, stream=None,
-                    active_rank_mask: Optional[int] = None) -> DispatchViews:
+                    active_rank_mask: Optional[int] = None, extra_payload=None,
+                    eplb_local_stats=None) -> DispatchViews:
     counts, cptr = _i32_array(num_tokens)
     views = DispatchViews()
     mask = None if active_rank_mask is None else C.byref(C.c_uint64(int(active_rank_mask)))
-    _check(lib.moe_ep_dispatch(handle, _ptr(hidden), _ptr(scales), _ptr(topk_ids),
+    _check(lib.moe_ep_dispatch(handle, _ptr(hidden), _ptr(scales), _ptr(extra_payload),
+                               _ptr(eplb_local_stats), _ptr(topk_ids),
                                _ptr(topk_weights), cptr, int(runtime_max_tokens_per_rank), mask,
                                _stream(stream), C.byref(views)))
     del counts
@@ -221,10 +229,12 @@ class MoeEpExchange:
     def __init__(self, ep_size: int, num_experts: int, top_k: int, max_tokens_per_rank: int,
                  hidden_size: int, dispatch_format="bf16", combine_format="bf16",
                  has_weights: bool = True, invalid_expert_id: Optional[int] = None,
+                 extra_payload_bytes_per_token: int = 0, eplb_stats_num_experts: int = 0,
                  device="cuda"):
         import torch
         self.params = make_params(ep_size, num_experts, top_k, max_tokens_per_rank, hidden_size,
-                                  dispatch_format, combine_format, has_weights, invalid_expert_id)
+                                  dispatch_format, combine_format, has_weights, invalid_expert_id,
+                                  extra_payload_bytes_per_token, eplb_stats_num_experts)
         self.size_per_rank = moe_ep_workspace_bytes(self.params)
         self.workspace = torch.empty((ep_size, self.size_per_rank), dtype=torch.uint8,
                                      device=device)
@@ -238,7 +248,8 @@ class MoeEpExchange:
     def row_bytes(self):
         """(payload row bytes, scale row bytes) of the dispatch format."""
         H, f = self.params.hidden_size, self.params.dispatch_format
-        return {FMT_BF16: (2 * H, 0), FMT_MXFP8: (H, H // 32), FMT_NVFP4: (H // 2, H // 16)}[f]
+        return {FMT_BF16: (2 * H, 0), FMT_MXFP8: (H, H // 32), FMT_NVFP4: (H // 2, H // 16),
+                FMT_DEEPSEEK_FP8: (H, H // 128 * 4)}[f]
 
     def destroy(self):
         if self.handle is not None:
@@ -263,7 +274,8 @@ class MoeEpExchange:
 
     def dispatch(self, hidden, topk_ids, topk_weights=None, scales=None, num_tokens=None,
                  runtime_max_tokens_per_rank: Optional[int] = None, stream=None,
-                 active_rank_mask: Optional[int] = None):
+                 active_rank_mask: Optional[int] = None, extra_payload=None,
+                 eplb_local_stats=None):
         import torch
         P = self.P
         T = runtime_max_tokens_per_rank or self.params.max_tokens_per_rank
@@ -286,11 +298,24 @@ class MoeEpExchange:
             _need(scales.dim() >= 2 and scales.shape[0] == P and scales.shape[1] == T and
                   scales.numel() * scales.element_size() == P * T * srow,
                   f"scales must be [P, T] rows of {srow} bytes")
+        if extra_payload is not None:
+            xb = self.params.extra_payload_bytes_per_token
+            _dev_contig(extra_payload, "extra_payload")
+            _need(extra_payload.dim() >= 2 and extra_payload.shape[0] == P and
+                  extra_payload.shape[1] == T and
+                  extra_payload.numel() * extra_payload.element_size() == P * T * xb,
+                  f"extra_payload must be [P, T] rows of {xb} bytes")
+        if eplb_local_stats is not None:
+            n = self.params.eplb_stats_num_experts
+            _dev_contig(eplb_local_stats, "eplb_local_stats")
+            _need(eplb_local_stats.dtype == torch.int32 and
+                  tuple(eplb_local_stats.shape) == (P, n),
+                  f"eplb_local_stats must be int32 [P, {n}]")
         if num_tokens is None:
             num_tokens = [T] * P
         _need(len(num_tokens) == P, "num_tokens needs one entry per rank")
         v = moe_ep_dispatch(self.handle, hidden, scales, topk_ids, topk_weights, num_tokens,
-                            T, stream, active_rank_mask)
+                            T, stream, active_rank_mask, extra_payload, eplb_local_stats)
         self.views = v
         k = self.params.top_k
         out = {
@@ -308,6 +333,12 @@ class MoeEpExchange:
                                         v.counts_offset).view(torch.int32)
         out["src_offsets"] = base.as_strided((P, (P + 1) * 4), (self.size_per_rank, 1),
                                              v.src_offsets_offset).view(torch.int32)
+        out["extra"] = self._plane(v.extra_offset, v.extra_row_bytes, T)
+        out["eplb_gathered_stats"] = None
+        if v.eplb_offset >= 0:
+            n = v.eplb_num_experts
+            out["eplb_gathered_stats"] = base.as_strided((P, P * n * 4), (self.size_per_rank, 1),
+                                                         v.eplb_offset).view(torch.int32).view(P, P, n)
         return out
 
     def combine_landing(self):

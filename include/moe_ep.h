@@ -79,6 +79,7 @@ extern "C" {
 #define MOE_EP_FMT_BF16 0  /* row = 2H bytes, no scale row               */
 #define MOE_EP_FMT_MXFP8 1 /* row = H e4m3 bytes, scale row = H/32 e8m0  */
 #define MOE_EP_FMT_NVFP4 2 /* row = H/2 packed e2m1, scale row = H/16 e4m3 */
+#define MOE_EP_FMT_DEEPSEEK_FP8 3 /* row = H e4m3, scale row = H/128 fp32 (1x128 blocks) */
 
 /* Combine payload formats. */
 #define MOE_EP_COMBINE_BF16 0
@@ -95,6 +96,8 @@ typedef struct moe_ep_params {
     int32_t combine_format;      /* MOE_EP_COMBINE_*                           */
     int32_t has_weights;         /* 1: top-k weights travel with tokens        */
     int32_t invalid_expert_id;   /* id written to empty slots (usually E)      */
+    int32_t extra_payload_bytes_per_token; /* >= 0: room for extra bytes per token */
+    int32_t eplb_stats_num_experts; /* >= 0: n of the EPLB statistics all-gather */
 } moe_ep_params;
 
 /* Where a dispatch's receive planes live.  Plane X of rank r starts at
@@ -116,6 +119,11 @@ typedef struct moe_ep_dispatch_views {
     int64_t src_offsets_offset;  /* [P+1] int32 exclusive prefix of counts; [P] = recv_total */
     int64_t combine_payload_offset; /* FP8 combine landing codes [P*T][H], or -1 */
     int64_t combine_scales_offset;  /* FP8 combine landing scales [P*T][H/32], or -1 */
+    int64_t extra_offset;        /* [P*T][extra_row_bytes] extra per-token bytes */
+    int64_t extra_row_bytes;     /* extra_payload_bytes_per_token (0: none)   */
+    int64_t eplb_offset;         /* [P][n] int32 gathered statistics (row s = rank s),
+                                    -1 when this dispatch carried none        */
+    int64_t eplb_num_experts;    /* n                                         */
 } moe_ep_dispatch_views;
 
 typedef struct moe_ep_handle moe_ep_handle;
@@ -141,7 +149,15 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
  *  hidden            device [P][T][payload_row_bytes], 16-byte aligned;
  *                    row t of rank s is token t of rank s
  *  scales            device [P][T][scale_row_bytes]; required for MXFP8 /
- *                    NVFP4, must be NULL for BF16
+ *                    NVFP4 / DeepSeekFp8, must be NULL for BF16
+ *  extra_payload     device [P][T][extra_payload_bytes_per_token] or NULL:
+ *                    more bytes per token, forwarded like the scale row
+ *                    (NVLinkOneSidedConfig, extra_payload_bytes_per_token)
+ *  eplb_local_stats  device [P][eplb_stats_num_experts] int32 or NULL: each
+ *                    rank's expert-load statistics; every live rank receives
+ *                    the [P][n] matrix (row s = rank s's statistics) in its
+ *                    region (moe_a2a_dispatch, eplb_local_stats ->
+ *                    eplb_gathered_stats)
  *  topk_ids          device [P][T][k] int32 global expert ids
  *  topk_weights      device [P][T][k] fp32; required iff has_weights
  *  num_tokens        host [P]: local_num_tokens n_s, 0 <= n_s <= T
@@ -161,6 +177,7 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
  * offsets and the ascending list of valid slots.
  */
 int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
+                    const void *extra_payload, const int32_t *eplb_local_stats,
                     const int32_t *topk_ids, const float *topk_weights,
                     const int32_t *num_tokens, int32_t runtime_max_tokens_per_rank,
                     const uint64_t *active_rank_mask, void *stream,

@@ -59,6 +59,13 @@ def test_workspace_bytes_layout(m):
     assert n8 > 4096 * (7168 + 224 + 64 + 4 + 7168 + 224)
     # no weights plane when has_weights = 0
     assert m.moe_ep_workspace_bytes(m.make_params(8, 256, 8, 128, 7168, has_weights=False)) == n - S * 32
+    # extra bytes and EPLB statistics add their planes
+    nx = m.moe_ep_workspace_bytes(m.make_params(8, 256, 8, 128, 7168, extra_payload_bytes_per_token=48,
+                                                eplb_stats_num_experts=256))
+    assert nx == n + S * 48 + 8 * 256 * 4
+    # DeepSeekFp8: H e4m3 bytes + H/128 fp32 scales per row
+    nd = m.moe_ep_workspace_bytes(m.make_params(8, 256, 8, 128, 7168, "deepseek_fp8"))
+    assert nd == n - S * 7168 + S * 56 * 4
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -71,6 +78,8 @@ def test_workspace_bytes_layout(m):
     (dict(hidden_size=7176, dispatch_format="mxfp8"), -1),
     (dict(hidden_size=7176, combine_format="fp8"), -1),
     (dict(dispatch_format=7), -2), (dict(combine_format=5), -2),
+    (dict(hidden_size=7200, dispatch_format="deepseek_fp8"), -1),  # H % 128
+    (dict(extra_payload_bytes_per_token=-1), -1), (dict(eplb_stats_num_experts=-4), -1),
     (dict(max_tokens_per_rank=1 << 30, ep_size=64), -4),
 ])
 def test_param_validation(m, kw, code):
@@ -96,12 +105,12 @@ def test_create_checks_workspace_before_device(m):
 
 def test_calls_on_bad_handles(m):
     counts = (C.c_int32 * 8)(*([1] * 8))
-    assert m.lib.moe_ep_dispatch(None, C.c_void_p(256), None, C.c_void_p(256), None, counts, 0,
-                                 None, None, None) == m.ERR_INVALID_ARG
+    assert m.lib.moe_ep_dispatch(None, C.c_void_p(256), None, None, None, C.c_void_p(256), None,
+                                 counts, 0, None, None, None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_combine(None, C.c_void_p(256), C.c_void_p(256), None) == m.ERR_INVALID_ARG
     bogus = C.c_void_p(0x1234560)
-    assert m.lib.moe_ep_dispatch(bogus, C.c_void_p(256), None, C.c_void_p(256), None, counts, 0,
-                                 None, None, None) == m.ERR_INVALID_ARG
+    assert m.lib.moe_ep_dispatch(bogus, C.c_void_p(256), None, None, None, C.c_void_p(256), None,
+                                 counts, 0, None, None, None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_destroy(None) == 0
     assert m.lib.moe_ep_destroy(bogus) == 0  # unknown handles are ignored
 

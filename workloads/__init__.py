@@ -31,6 +31,7 @@ import numpy as np
 FMT_BF16 = "bf16"
 FMT_MXFP8 = "mxfp8"
 FMT_NVFP4 = "nvfp4"
+FMT_DEEPSEEK_FP8 = "deepseek_fp8"
 
 
 @dataclasses.dataclass(frozen=True)
@@ -106,6 +107,8 @@ def payload_row_bytes(fmt: str, H: int) -> int:
         return H
     if fmt == FMT_NVFP4:
         return H // 2
+    if fmt == FMT_DEEPSEEK_FP8:
+        return H
     raise ValueError(fmt)
 
 
@@ -117,6 +120,8 @@ def scale_row_bytes(fmt: str, H: int) -> int:
         return H // 32
     if fmt == FMT_NVFP4:
         return H // 16
+    if fmt == FMT_DEEPSEEK_FP8:
+        return H // 128 * 4
     raise ValueError(fmt)
 
 
@@ -256,6 +261,20 @@ def encode_nvfp4(x_bf16):
     return packed.contiguous(), scales.contiguous()
 
 
+def encode_deepseek_fp8(x_bf16):
+    """DeepSeekFp8 payload of bf16 rows ``[..., H]``: e4m3 codes ``[..., H]``
+    and one fp32 scale per 128 elements ``[..., H/128]`` as bytes
+    ``[..., H/32]``: scale = amax / 448, element = e4m3(x / scale)."""
+    torch = _torch()
+    H = x_bf16.shape[-1]
+    xb = x_bf16.float().reshape(*x_bf16.shape[:-1], H // 128, 128)
+    amax = xb.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+    codes = (xb / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
+    scales = scale.reshape(*x_bf16.shape[:-1], H // 128).contiguous().view(torch.uint8)
+    return codes.reshape(x_bf16.shape).contiguous(), scales
+
+
 @dataclasses.dataclass
 class DispatchInputs:
     routing: Routing
@@ -279,6 +298,8 @@ def draw_dispatch_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
         payload, scales = encode_mxfp8(hidden)
     elif w.fmt == FMT_NVFP4:
         payload, scales = encode_nvfp4(hidden)
+    elif w.fmt == FMT_DEEPSEEK_FP8:
+        payload, scales = encode_deepseek_fp8(hidden)
     else:
         raise ValueError(w.fmt)
     return DispatchInputs(routing, payload, scales, hidden)
