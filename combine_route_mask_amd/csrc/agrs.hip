@@ -13,8 +13,6 @@
 namespace moe_ep {
 namespace {
 
-constexpr int kVpt = 2;
-
 // Rank whose segment [off[q], off[q+1]) holds global row j (empty segments
 // are skipped).  Uniform across the workgroup.
 __device__ __forceinline__ int segment_of(const int32_t *off, int P, int64_t j)
@@ -69,56 +67,74 @@ __global__ __launch_bounds__(kBlock) void allgatherv_kernel(AllGatherArgs a, int
     }
 }
 
-__global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterArgs a, int64_t rows)
+#ifndef MOE_EP_RS_GATHER
+#define MOE_EP_RS_GATHER 8 // ranks whose rows a reduce-scatterv lane loads at once
+#endif
+#ifndef MOE_EP_RS_VPT
+#define MOE_EP_RS_VPT 1    // 16-byte vectors per lane per row chunk
+#endif
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// Item (global row j, chunk c): each lane owns VPT 16-byte vectors of the
+// output row and sums, in fp32 and ascending rank order, those vectors of
+// row j of every rank's partial, with the loads of G ranks in flight at
+// once; the owner of row j keeps the bf16 result.
+template <int VPT, int G>
+__global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterArgs a, int64_t rows,
+                                                                 int64_t nchunk)
 {
     const int64_t nvec = a.H >> 3;
-    for (int64_t j = blockIdx.x; j < rows; j += gridDim.x) {
+    for (int64_t w = blockIdx.x; w < rows * nchunk; w += gridDim.x) {
+        const int64_t j = w / nchunk, c = w % nchunk;
+        const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
+        if (i0 >= nvec)
+            continue;
         const int r = segment_of(a.off, a.P, j);
         const int64_t i = j - a.off[r];
-        for (int64_t b = 0; b < nvec; b += kBlock * kVpt) {
-            float acc[kVpt][8];
+        bool in[VPT];
 #pragma unroll
-            for (int u = 0; u < kVpt; ++u)
+        for (int u = 0; u < VPT; ++u)
+            in[u] = i0 + u * kBlock < nvec;
+        float acc[VPT][8];
 #pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    acc[u][e] = 0.0f;
-            for (int q = 0; q < a.P; ++q) {
-                const uint4 *src = reinterpret_cast<const uint4 *>(a.in + (int64_t)q * a.in_stride + j * a.H);
-                uint4 v[kVpt];
+        for (int u = 0; u < VPT; ++u)
 #pragma unroll
-                for (int u = 0; u < kVpt; ++u) {
-                    const int64_t k = b + u * kBlock + threadIdx.x;
-                    if (k < nvec)
-                        v[u] = src[k];
-                }
+            for (int e = 0; e < 8; ++e)
+                acc[u][e] = 0.0f;
+        for (int q0 = 0; q0 < a.P; q0 += G) {
+            u32x4 v[G][VPT];
 #pragma unroll
-                for (int u = 0; u < kVpt; ++u) {
-                    const int64_t k = b + u * kBlock + threadIdx.x;
-                    if (k < nvec) {
-                        const uint32_t w[4] = {v[u].x, v[u].y, v[u].z, v[u].w};
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+                    if (q0 + g < a.P && in[u])
+                        v[g][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
+                            a.in + (int64_t)(q0 + g) * a.in_stride + j * a.H + (i0 + u * kBlock) * 8));
+#pragma unroll
+            for (int g = 0; g < G; ++g)
+#pragma unroll
+                for (int u = 0; u < VPT; ++u)
+                    if (q0 + g < a.P && in[u]) {
 #pragma unroll
                         for (int e = 0; e < 4; ++e) {
                             float lo, hi;
-                            unpack_bf16x2(w[e], lo, hi);
+                            unpack_bf16x2(v[g][u][e], lo, hi);
                             acc[u][2 * e] += lo;
                             acc[u][2 * e + 1] += hi;
                         }
                     }
-                }
-            }
-            uint4 *dst = reinterpret_cast<uint4 *>(a.out + (int64_t)r * a.out_stride + i * a.H);
+        }
 #pragma unroll
-            for (int u = 0; u < kVpt; ++u) {
-                const int64_t k = b + u * kBlock + threadIdx.x;
-                if (k < nvec) {
-                    uint4 o;
-                    o.x = pack_bf16x2(acc[u][0], acc[u][1]);
-                    o.y = pack_bf16x2(acc[u][2], acc[u][3]);
-                    o.z = pack_bf16x2(acc[u][4], acc[u][5]);
-                    o.w = pack_bf16x2(acc[u][6], acc[u][7]);
-                    dst[k] = o;
-                }
-            }
+        for (int u = 0; u < VPT; ++u) {
+            if (!in[u])
+                continue;
+            u32x4 o;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                o[e] = pack_bf16x2(acc[u][2 * e], acc[u][2 * e + 1]);
+            *reinterpret_cast<u32x4 *>(a.out + (int64_t)r * a.out_stride + i * a.H +
+                                       (i0 + u * kBlock) * 8) = o;
         }
     }
 }
@@ -139,7 +155,9 @@ hipError_t launch_allgatherv(const AllGatherArgs &a, int64_t rows, hipStream_t s
 
 hipError_t launch_reduce_scatterv(const ReduceScatterArgs &a, int64_t rows, hipStream_t s)
 {
-    hipLaunchKernelGGL(reduce_scatterv_kernel, dim3(grid_for(rows)), dim3(kBlock), 0, s, a, rows);
+    const int64_t nchunk = ((a.H >> 3) + kBlock * MOE_EP_RS_VPT - 1) / (kBlock * MOE_EP_RS_VPT);
+    hipLaunchKernelGGL((reduce_scatterv_kernel<MOE_EP_RS_VPT, MOE_EP_RS_GATHER>),
+                       dim3(grid_for(rows * nchunk)), dim3(kBlock), 0, s, a, rows, nchunk);
     return hipGetLastError();
 }
 
