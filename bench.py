@@ -285,9 +285,11 @@ def _time(fn, iters):
 
 def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     """Step time of `steps` dispatch+combine steps after `warmup` untimed
-    ones, eager (two C-ABI launches per step) and as one HIP-graph replay
-    per step; per-launch kernel times from graphs of 20 back-to-back
-    launches of one kernel.  All events sit on the launch stream."""
+    ones, eager (two C-ABI launches per step) and from HIP-graph replays of
+    10 steps each; per-launch kernel times from graphs of 20 back-to-back
+    launches of one kernel.  With flush_bytes, every timed step and every
+    timed single launch follows a fill of that many bytes (last-level
+    cache cold) and is timed alone.  All events sit on the launch stream."""
     import torch
 
     def step():
@@ -312,7 +314,7 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
                 "combine_ms": _time(setup.combine, steps) / steps, "wall_s": 0.0}
     # one graph holds `per` consecutive steps, so a small step is not bound
     # by the host's graph-launch rate; `steps` is rounded up to a multiple
-    per = 1 if flush_bytes else 10
+    per = 10
     replays = -(-steps // per)
     g_step = _graph(step, per)
     for _ in range(max(1, warmup // per)):
@@ -324,10 +326,11 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
         stream = torch.cuda.current_stream()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
+        # eager launches: the host enqueues them while the fill still runs
         for i in range(steps):
             flush.fill_(i & 0xFF)
             ev[i][0].record(stream)
-            g_step.replay()
+            step()
             ev[i][1].record(stream)
         torch.cuda.synchronize()
         graph_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
@@ -340,6 +343,24 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
         assert torch.equal(setup.out.view(torch.int16), ref_out.view(torch.int16))
         assert torch.equal(setup.views["ids"], ref_ids)
 
+    if flush_bytes:
+        # cold per-kernel times: the same fill before each single launch
+        flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        stream = torch.cuda.current_stream()
+        per_kernel = []
+        for fn in (setup.dispatch, setup.combine):
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(steps)]
+            for i in range(steps):
+                flush.fill_(i & 0xFF)
+                ev[i][0].record(stream)
+                fn()
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            per_kernel.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
+        del flush, g_step
+        return {"ms_per_step": graph_ms, "eager_ms_per_step": eager_ms, "dispatch_ms": per_kernel[0],
+                "combine_ms": per_kernel[1], "wall_s": wall}
     reps = 20
     g_d = _graph(setup.dispatch, reps)
     g_c = _graph(setup.combine, reps)
@@ -435,8 +456,9 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ep8", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="ep64,ep8-mxfp8,agrs",
-                    help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--also", default="ep8-cold,ep64,ep8-mxfp8,agrs",
+                    help="comma list of extra workloads ('' for none); a '-cold' suffix flushes "
+                         "the last-level cache between steps")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--cold", action="store_true", help="flush the last-level cache between steps")
@@ -487,14 +509,17 @@ def main():
 
     also = []
     for name in [a for a in args.also.split(",") if a]:
-        if name == args.config:
+        cold = args.cold or name.endswith("-cold")
+        base = name[:-5] if name.endswith("-cold") else name
+        if base == args.config and cold == args.cold:
             continue
-        wa = WORKLOADS[name]
-        print(f"[bench] setting up {wa.name}", file=sys.stderr, flush=True)
-        sa = AgRsSetup(wa) if name == "agrs" else Setup(wa)
+        wa = WORKLOADS[base]
+        print(f"[bench] setting up {wa.name}{' (cold)' if cold else ''}", file=sys.stderr, flush=True)
+        sa = AgRsSetup(wa) if base == "agrs" else Setup(wa)
         ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2),
-                     flush_bytes=(1 << 30) if args.cold else 0, graphs=not args.no_graph)
+                     flush_bytes=(1 << 30) if cold else 0, graphs=not args.no_graph)
         ra, _ = summarize(sa, ma)
+        ra["cache"] = "cold" if cold else "warm"
         sa.free()
         del sa
         torch.cuda.empty_cache()
