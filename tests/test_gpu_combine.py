@@ -67,6 +67,7 @@ SMALL = [
     dataclasses.replace(W.TINY, name="long rows H8200", P=3, E=12, k=4, T=6, H=8200, n_lo=1, n_hi=6),
     dataclasses.replace(W.TINY, name="k1", k=1, T=70, H=512, n_lo=1, n_hi=70),
     dataclasses.replace(W.EP8_BF16, name="ep8 mid", T=40, H=1024, n_lo=0, n_hi=40),
+    dataclasses.replace(W.TINY, name="k16", P=8, E=64, k=16, T=30, H=512, n_lo=0, n_hi=30),
 ]
 
 

@@ -92,6 +92,8 @@ SMALL = [
     dataclasses.replace(W.EP64_NVFP4, name="nvfp4 small", P=16, E=64, T=20, H=64, n_lo=3, n_hi=20),
     dataclasses.replace(W.TINY, name="many slots P16 T1500", P=16, E=64, k=4, T=1500, H=32,
                         n_lo=700, n_hi=1500),
+    dataclasses.replace(W.TINY, name="k16", P=8, E=64, k=16, T=50, H=256, n_lo=0, n_hi=50),
+    dataclasses.replace(W.TINY, name="k64 all experts", P=4, E=64, k=64, T=20, H=128, n_lo=0, n_hi=20),
 ]
 
 
@@ -100,6 +102,27 @@ SMALL = [
 def test_dispatch_small(w, seed):
     c = random_byte_case(w, seed, oob=(seed == 12), dup=(seed == 12))
     _run(c)
+
+
+@pytest.mark.parametrize("k", [4, 8, 16])
+def test_dispatch_ids_not_16_byte_aligned(k):
+    # id / weight planes that start 4 bytes past a 16-byte boundary take the
+    # word-wise id path; results must not change
+    w = dataclasses.replace(W.TINY, name=f"unaligned k{k}", P=8, E=64, k=k, T=30, H=128, n_lo=0, n_hi=30)
+    c = random_byte_case(w, 21, oob=True, dup=True)
+    log(f"dispatch case: {w.name} with 4-byte-offset id and weight planes")
+    pl, sc, ids, wt = gpu_inputs(c)
+    n = ids.numel()
+    ids_buf = torch.empty(n + 1, dtype=torch.int32, device=ids.device)
+    wt_buf = torch.empty(n + 1, dtype=torch.float32, device=wt.device)
+    ids_u = ids_buf[1:].view(ids.shape)
+    wt_u = wt_buf[1:].view(wt.shape)
+    ids_u.copy_(ids)
+    wt_u.copy_(wt)
+    assert ids_u.data_ptr() % 16 != 0 and wt_u.data_ptr() % 16 != 0
+    ex = _exchange(w)
+    out = ex.dispatch(pl, ids_u, wt_u, num_tokens=c.counts.tolist(), runtime_max_tokens_per_rank=w.T)
+    _check(c, out)
 
 
 def test_dispatch_without_weights_and_custom_marker():
