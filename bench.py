@@ -11,6 +11,9 @@ eager two-launch time is reported beside it).  Prints one JSON line:
                average launch time (HIP events on the launch stream),
                against the MI355X HBM peak (8 TB/s)
   cpu_baseline the CPU oracle on a bounded sample of the same workload
+  also         the other workloads (--also); a '-cold' entry writes 1 GiB
+               and reads another 1 GiB before every timed step and launch,
+               so the last-level cache holds none of the step's data
 
 Algorithmic bytes (per launch; N tokens, M (token, destination) pairs,
 row / srow payload and scale row bytes, k, P ranks, T tokens per rank):
@@ -283,13 +286,30 @@ def _time(fn, iters):
     return a.elapsed_time(b)
 
 
+class _Flush:
+    """Evicts the last-level cache: writes nbytes of one scratch buffer,
+    then reads nbytes of another, so the cache ends up holding clean lines
+    of unrelated data (no dirty write-backs land in the timed region)."""
+
+    def __init__(self, nbytes):
+        import torch
+        self.w = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+        self.r = torch.zeros(nbytes // 4, dtype=torch.int32, device="cuda")
+        self.i = 0
+
+    def __call__(self):
+        self.i += 1
+        self.w.fill_(self.i & 0xFF)
+        self.sink = self.r.max()
+
+
 def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     """Step time of `steps` dispatch+combine steps after `warmup` untimed
     ones, eager (two C-ABI launches per step) and from HIP-graph replays of
     10 steps each; per-launch kernel times from graphs of 20 back-to-back
     launches of one kernel.  With flush_bytes, every timed step and every
-    timed single launch follows a fill of that many bytes (last-level
-    cache cold) and is timed alone.  All events sit on the launch stream."""
+    timed single launch follows a write and a read of that many bytes
+    (last-level cache cold and clean) and is timed alone.  All events sit on the launch stream."""
     import torch
 
     def step():
@@ -321,14 +341,15 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
         g_step.replay()
     wall0 = time.perf_counter()
     if flush_bytes:
-        # cold: a 1 GiB fill between steps (untimed) evicts the last-level cache
-        flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        # cold: a 1 GiB write, then a 1 GiB read of another buffer, between
+        # steps (untimed) evicts the last-level cache
+        flush = _Flush(flush_bytes)
         stream = torch.cuda.current_stream()
         ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
               for _ in range(steps)]
-        # eager launches: the host enqueues them while the fill still runs
+        # eager launches: the host enqueues them while the flush still runs
         for i in range(steps):
-            flush.fill_(i & 0xFF)
+            flush()
             ev[i][0].record(stream)
             step()
             ev[i][1].record(stream)
@@ -345,14 +366,14 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
 
     if flush_bytes:
         # cold per-kernel times: the same fill before each single launch
-        flush = torch.empty(flush_bytes, dtype=torch.uint8, device="cuda")
+        flush = _Flush(flush_bytes)
         stream = torch.cuda.current_stream()
         per_kernel = []
         for fn in (setup.dispatch, setup.combine):
             ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                   for _ in range(steps)]
             for i in range(steps):
-                flush.fill_(i & 0xFF)
+                flush()
                 ev[i][0].record(stream)
                 fn()
                 ev[i][1].record(stream)
@@ -445,9 +466,17 @@ def cpu_baseline(w, budget_s=12.0):
         el = time.perf_counter() - t0
         if el >= budget_s:
             break
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
+    except OSError:
+        pass
     return {"value": N * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{steps} full dispatch+combine steps of '{w.name}' ({N} tokens each), "
-                      f"single-threaded C oracle, {el:.1f} s"}
+                      f"single-threaded C oracle, {el:.1f} s",
+            "host": {"cpu": model, "nproc": os.cpu_count(),
+                     "usable_cpus": len(os.sched_getaffinity(0))}}
 
 
 def main():
@@ -456,7 +485,7 @@ def main():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="ep8", choices=sorted(WORKLOADS))
-    ap.add_argument("--also", default="ep8-cold,ep64,ep8-mxfp8,agrs",
+    ap.add_argument("--also", default="ep8-cold,ep64,ep64-cold,ep64-nvfp4,ep8-mxfp8,agrs",
                     help="comma list of extra workloads ('' for none); a '-cold' suffix flushes "
                          "the last-level cache between steps")
     ap.add_argument("--no-graph", action="store_true",
