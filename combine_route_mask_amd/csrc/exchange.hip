@@ -22,8 +22,17 @@
 #ifndef MOE_EP_NT_STORE
 #define MOE_EP_NT_STORE 1     // dispatch row stores bypass the caches' retention
 #endif
-#ifndef MOE_EP_DISPATCH_VPT
-#define MOE_EP_DISPATCH_VPT 4 // 16-byte vectors per thread in a dispatch row chunk
+// 16-byte vectors per thread in a dispatch row chunk, for payload rows of at
+// least MOE_EP_DISPATCH_LONG_ROW bytes and for shorter ones (short rows split
+// into more, smaller chunks so more workgroups share a step's few rows).
+#ifndef MOE_EP_DISPATCH_VPT_LONG
+#define MOE_EP_DISPATCH_VPT_LONG 4
+#endif
+#ifndef MOE_EP_DISPATCH_VPT_SHORT
+#define MOE_EP_DISPATCH_VPT_SHORT 1
+#endif
+#ifndef MOE_EP_DISPATCH_LONG_ROW
+#define MOE_EP_DISPATCH_LONG_ROW 8192
 #endif
 #ifndef MOE_EP_DISPATCH_NT_LOAD
 #define MOE_EP_DISPATCH_NT_LOAD 0 // dispatch reads each token row once
@@ -33,9 +42,11 @@
 #endif
 // BF16 combine shapes: (16-byte vectors per thread, ranks loaded at once,
 // non-temporal output stores) for outputs that fit the 256 MB last-level
-// cache and for larger ones.
+// cache and for larger ones.  Output rows are not read again within a step,
+// so both store them non-temporally (which also leaves the cache to the next
+// dispatch's rows).
 #ifndef MOE_EP_COMBINE_SMALL
-#define MOE_EP_COMBINE_SMALL 1, 8, 0
+#define MOE_EP_COMBINE_SMALL 1, 8, 1
 #endif
 #ifndef MOE_EP_COMBINE_LARGE
 #define MOE_EP_COMBINE_LARGE 4, 2, 1
@@ -60,8 +71,6 @@ constexpr int kScanUnroll = MOE_EP_SCAN_UNROLL; // 256-slot chunks per scan step
 constexpr int kWaves = kBlock / 64;
 constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
 constexpr int kPlaneGroup = 8;          // destinations per id-plane item
-constexpr int kDVpt = MOE_EP_DISPATCH_VPT;
-constexpr int kDChunk = kBlock * kDVpt; // 16-byte vectors per dispatch row chunk
 
 __device__ __forceinline__ u32x4 load16_nt(const void *p)
 {
@@ -343,10 +352,10 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
     __syncthreads(); // smask is reused by the block's next item
 }
 
-// Chunk c of token q's payload row (kDVpt 16-byte vectors per thread, lane
+// Chunk c of token q's payload row (DV 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
 // chunk 0 also carries the scale row and the extra payload bytes.
-template <int KQ>
+template <int KQ, int DV>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
@@ -357,12 +366,12 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
     if (!mask)
         return;
     const int64_t nvec = a.row_bytes >> 4;
-    const int64_t i0 = c * kDChunk + threadIdx.x;
+    const int64_t i0 = c * (kBlock * DV) + threadIdx.x;
     const uint8_t *src = a.payload + q * a.row_bytes;
     uint8_t *dst0 = a.ws + a.off_payload + q * a.row_bytes;
-    u32x4 v[kDVpt];
+    u32x4 v[DV];
 #pragma unroll
-    for (int u = 0; u < kDVpt; ++u)
+    for (int u = 0; u < DV; ++u)
         if (i0 + u * kBlock < nvec)
 #if MOE_EP_DISPATCH_NT_LOAD
             v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16));
@@ -375,7 +384,7 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
         m &= m - 1;
         uint8_t *d = dst0 + (int64_t)r * a.region;
 #pragma unroll
-        for (int u = 0; u < kDVpt; ++u)
+        for (int u = 0; u < DV; ++u)
             if (i0 + u * kBlock < nvec)
                 store16(d + (i0 + u * kBlock) * 16, v[u]);
     }
@@ -392,8 +401,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 //   [P, P + plane_blocks)     id / weight planes, (destination group, slot chunk) items
 //   [P + plane_blocks, grid)  payload scatter, (token, row chunk) items
 // The last two roles loop over their items when there are more items than
-// blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k).
-template <int KQ>
+// blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
+// DV: 16-byte vectors per thread in a payload row chunk.
+template <int KQ, int DV>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
 {
@@ -414,7 +424,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     const int64_t first = a.P + plane_blocks;
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
-        scatter_chunk<KQ>(a, w / nchunk, w % nchunk);
+        scatter_chunk<KQ, DV>(a, w / nchunk, w % nchunk);
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
@@ -720,11 +730,17 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t nplane = ceil_div(S, kPlaneSlots);
     const int64_t plane_blocks = grid_for(ceil_div(a.P, kPlaneGroup) * nplane);
-    const int64_t nchunk = ceil_div(a.row_bytes >> 4, kDChunk);
+    const bool long_rows = a.row_bytes >= MOE_EP_DISPATCH_LONG_ROW;
+    const int dv = long_rows ? MOE_EP_DISPATCH_VPT_LONG : MOE_EP_DISPATCH_VPT_SHORT;
+    const int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
     const int64_t grid =
         a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
-    hipLaunchKernelGGL(dispatch_kernel<KQ>, dim3((unsigned)grid), dim3(kBlock), 0, s, a, nplane,
-                       plane_blocks, nchunk);
+    if (long_rows)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG>), dim3((unsigned)grid),
+                           dim3(kBlock), 0, s, a, nplane, plane_blocks, nchunk);
+    else
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT>), dim3((unsigned)grid),
+                           dim3(kBlock), 0, s, a, nplane, plane_blocks, nchunk);
     return hipGetLastError();
 }
 
