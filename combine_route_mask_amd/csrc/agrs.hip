@@ -133,8 +133,9 @@ __global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterAr
 #pragma unroll
             for (int e = 0; e < 4; ++e)
                 o[e] = pack_bf16x2(acc[u][2 * e], acc[u][2 * e + 1]);
-            *reinterpret_cast<u32x4 *>(a.out + (int64_t)r * a.out_stride + i * a.H +
-                                       (i0 + u * kBlock) * 8) = o;
+            // the output is not read again here: keep it out of the caches
+            __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(a.out + (int64_t)r * a.out_stride +
+                                                                    i * a.H + (i0 + u * kBlock) * 8));
         }
     }
 }
