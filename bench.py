@@ -472,7 +472,9 @@ def cpu_baseline(w, budget_s=12.0):
             model = next((ln.split(":", 1)[1].strip() for ln in f if ln.startswith("model name")), model)
     except OSError:
         pass
+    b = step_bytes(w, N, pair_count(w, R))
     return {"value": N * steps / el, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "GBps": (b["dispatch"] + b["combine"]) * steps / el / 1e9,
             "sample": f"{steps} full dispatch+combine steps of '{w.name}' ({N} tokens each), "
                       f"single-threaded C oracle, {el:.1f} s",
             "host": {"cpu": model, "nproc": os.cpu_count(),
