@@ -538,24 +538,32 @@ def main():
                 "bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
                 "frac_of_measured_copy": achieved / calib["copy_GBps"]}
 
-    also = []
+    # the other workloads; warm and cold runs of one workload share its
+    # buffers, so the two differ only in what the cache holds
+    plan = {}
     for name in [a for a in args.also.split(",") if a]:
         cold = args.cold or name.endswith("-cold")
         base = name[:-5] if name.endswith("-cold") else name
         if base == args.config and cold == args.cold:
             continue
+        if cold not in plan.setdefault(base, []):
+            plan[base].append(cold)
+    also = []
+    for base, colds in plan.items():
         wa = WORKLOADS[base]
-        print(f"[bench] setting up {wa.name}{' (cold)' if cold else ''}", file=sys.stderr, flush=True)
+        print(f"[bench] setting up {wa.name}", file=sys.stderr, flush=True)
         sa = AgRsSetup(wa) if base == "agrs" else Setup(wa)
-        ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2),
-                     flush_bytes=(1 << 30) if cold else 0, graphs=not args.no_graph)
-        ra, _ = summarize(sa, ma)
-        ra["cache"] = "cold" if cold else "warm"
+        for cold in colds:
+            ma = measure(sa, max(10, args.steps // 2), max(3, args.warmup // 2),
+                         flush_bytes=(1 << 30) if cold else 0, graphs=not args.no_graph)
+            ra, _ = summarize(sa, ma)
+            ra["cache"] = "cold" if cold else "warm"
+            print(f"[bench] {wa.name} ({ra['cache']}): {ra['ms_per_step']*1e3:.1f} us/step",
+                  file=sys.stderr, flush=True)
+            also.append(ra)
         sa.free()
         del sa
         torch.cuda.empty_cache()
-        print(f"[bench] {wa.name}: {ra['ms_per_step']*1e3:.1f} us/step", file=sys.stderr, flush=True)
-        also.append(ra)
 
     cpu = None
     if not args.no_cpu_baseline:
