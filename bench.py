@@ -98,13 +98,13 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str):
         f.write("# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE in KiB per\n"
                 "# dispatch), each scaled by its reading for a plain 2 GiB device copy\n"
                 "# (calibration copy in bench.py: 2 GiB read, 2 GiB written).  Commands, run from /tmp\n"
-                "# with TMPDIR=/tmp:\n"
-                "#   rocprofv3 --pmc FETCH_SIZE -d <repo>/gpurun_out/pmc_fetch -o pmc --output-format csv -- \\\n"
+                "# with TMPDIR=/tmp (<repo>: this repository, <out>: any output directory):\n"
+                "#   rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_fetch -o pmc --output-format csv -- \\\n"
                 "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
-                "#   rocprofv3 --pmc WRITE_SIZE -d <repo>/gpurun_out/pmc_write -o pmc --output-format csv -- \\\n"
+                "#   rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_write -o pmc --output-format csv -- \\\n"
                 "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
-                "#   python3 <repo>/bench.py --pmc-summary <repo>/gpurun_out/pmc_fetch/pmc_counter_collection.csv \\\n"
-                "#       <repo>/gpurun_out/pmc_write/pmc_counter_collection.csv\n"
+                "#   python3 <repo>/bench.py --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
+                "#       <out>/pmc_write/pmc_counter_collection.csv\n"
                 "# source_digest: first 16 hex digits of sha256(combine_route_mask_amd/csrc/exchange.hip)\n")
         for l in lines:
             f.write(l + "\n")
