@@ -49,7 +49,11 @@
  * The library allocates no device memory.  A handle keeps the last
  * dispatch's step size and per-rank token counts; combine uses them.
  * Handles are not thread-safe.  All launches go to the caller's stream,
- * in stream order, with no host synchronisation.
+ * in stream order, with no host synchronisation, and may be captured into
+ * a HIP graph: the host-side arguments of a call (per-rank token counts,
+ * the step size, the active rank mask, buffer pointers) are fixed into the
+ * captured launches, so a graph replays exactly the calls it captured and
+ * must be captured again when they change.
  *
  * Errors: every entry point validates all arguments before launching
  * anything (no partial launches) and returns one of the MOE_EP_* codes
