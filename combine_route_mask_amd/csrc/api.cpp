@@ -99,7 +99,7 @@ int check_params(const moe_ep_params *pp, Layout *lay)
         return fail(MOE_EP_ERR_UNSUPPORTED, "unknown dispatch_format");
     if (p.dispatch_format == MOE_EP_FMT_BF16 && p.hidden_size % 8 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG,
-                    "BF16 payload rows must be multiples of 16 bytes (hidden_size % 8 == 0)");
+                    "a BF16 payload row must be a whole number of 16-byte units (hidden_size % 8 == 0)");
     if (p.dispatch_format != MOE_EP_FMT_BF16 && p.hidden_size % 32 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG,
                     "MXFP8 / NVFP4 payloads need hidden_size % 32 == 0 (16-byte rows, whole scale blocks)");

@@ -8,26 +8,28 @@
  *
  * Semantics follow these documentation pages:
  *  - FlashInfer "flashinfer.moe_ep.NVLinkTwoSidedAlltoAll": dispatch()
- *    sends each token to the ranks owning its selected experts, with its
- *    top-k ids, top-k weights and per-token scale rows; combine() returns
- *    each token's per-rank expert outputs (already weighted and reduced
- *    over a rank's local experts) summed over ranks; destroy() is
+ *    delivers every token to each rank that holds one of its chosen
+ *    experts, together with the token's top-k ids, top-k weights and scale
+ *    row; combine() adds up, over ranks, each token's expert outputs
+ *    (already weighted and reduced over a rank's local experts); destroy() is
  *    idempotent; is_platform_supported() performs no collective work.
  *  - FlashInfer "flashinfer.moe_ep.NVLinkOneSidedConfig", lamport
- *    paragraph: the row a rank receives from rank src for src's token t
- *    sits at slot src * tokens_per_rank + t, tokens_per_rank being the
- *    step's runtime_max_tokens_per_rank; BF16, MXFP8 and NVFP4 dispatch
- *    formats; at most 64 EP ranks.  First options paragraph:
- *    use_low_precision_combine sends combine payloads as FP8.  cft
- *    paragraph: payload rows are multiples of 16 bytes.
+ *    paragraph: token t of rank src lands in slot src * tokens_per_rank + t
+ *    of a receiving rank, where tokens_per_rank equals the step's
+ *    runtime_max_tokens_per_rank; BF16, MXFP8 and NVFP4 dispatch formats;
+ *    at most 64 EP ranks.  First options paragraph: with
+ *    use_low_precision_combine the combine moves its rows as FP8 values.
+ *    cft paragraph: a payload row's size is a whole number of 16-byte
+ *    units.
  *  - FlashInfer "flashinfer.comm.moe_a2a_dispatch": runtime_max_tokens_per_rank
  *    may not exceed the capacity given at initialisation; the outputs are
- *    workspace-backed views, one per payload, plus the workspace offset
- *    reserved for the matching combine.
+ *    views into the workspace, one per payload, and the workspace offset
+ *    that the combine of the same step will use.
  *  - vLLM "device_communicators.all2all", FlashInferNVLinkTwoSidedManager:
  *    MoEEpCommParams(num_experts, top_k, max_tokens_per_rank, hidden_size,
- *    invalid_expert_id=num_experts); received rows that carry no token keep
- *    expert id invalid_expert_id, which no rank owns.
+ *    invalid_expert_id=num_experts); a received row without a token is
+ *    marked with expert id invalid_expert_id, an id outside every rank's
+ *    range.
  *  - vLLM "device_communicators.all2all", AgRsAll2AllManager: dispatch is
  *    all_gatherv of [hidden, topk_weights, topk_ids] along dim 0 with
  *    per-rank sizes; combine is reduce_scatterv of the hidden rows with

@@ -11,22 +11,23 @@
  *
  * Sources (FlashInfer and vLLM API documentation pages):
  *  - FlashInfer "flashinfer.moe_ep.NVLinkTwoSidedAlltoAll", dispatch():
- *    each token is sent to the ranks that own its selected experts; its
- *    global top-k ids, top-k weights and per-token scale rows travel with
- *    it, row-aligned.
+ *    a token is delivered to every rank holding one of its chosen experts,
+ *    and its global top-k ids, top-k weights and scale row go along with it
+ *    in the same slot.
  *  - FlashInfer "flashinfer.moe_ep.NVLinkOneSidedConfig", lamport
- *    paragraph: rows a rank receives from rank src for its token t sit at
- *    src * tokens_per_rank + t, tokens_per_rank being the step's
+ *    paragraph: token t of rank src occupies slot src * tokens_per_rank + t
+ *    of a receiving rank, with tokens_per_rank equal to the step's
  *    runtime_max_tokens_per_rank.
  *  - vLLM "device_communicators.all2all", FlashInferNVLinkTwoSidedManager
- *    (MoEEpCommParams(invalid_expert_id=num_experts)): received rows past
- *    a source rank's token count carry expert id num_experts, which no
- *    rank owns.
+ *    (MoEEpCommParams(invalid_expert_id=num_experts)): a received slot
+ *    beyond the sending rank's token count is marked with expert id
+ *    num_experts, outside every rank's range.
  *  - FlashInfer "NVLinkTwoSidedAlltoAll", combine(): each token's expert
  *    outputs, already weighted and reduced over a rank's local experts,
  *    summed over ranks into a [local_num_tokens, hidden] result.
  *  - FlashInfer "NVLinkOneSidedConfig", first options paragraph:
- *    use_low_precision_combine sends combine payloads as FP8.
+ *    with use_low_precision_combine the combine moves its rows as FP8
+ *    values.
  *  - vLLM "device_communicators.all2all", AgRsAll2AllManager.dispatch /
  *    combine: all_gatherv of [hidden, topk_weights, topk_ids] over ranks
  *    in rank order, and reduce_scatterv of the hidden rows by the same
@@ -47,8 +48,9 @@
  *    "moe_a2a_dispatch", eplb_local_stats / eplb_gathered_stats): row r of
  *    the gathered [ep_size, n] matrix holds rank r's statistics;
  *  - active rank mask (FlashInfer "flashinfer.comm.moe_a2a_dispatch",
- *    active_rank_mask parameter: tokens routed to a masked-off rank are
- *    dropped): with every virtual rank in one call, a masked-off rank
+ *    active_rank_mask parameter: a token bound for a rank whose bit is
+ *    clear never reaches it): with every virtual rank in one call, a
+ *    masked-off rank
  *    neither sends nor receives; nothing is written into its receive
  *    planes and combine produces no rows for it;
  *  - the FP8 combine payload is OCP e4m3fn with one power-of-two (e8m0)

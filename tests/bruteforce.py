@@ -2,11 +2,12 @@
 
 Written as a *push*: every source token is walked once and its row is
 appended to a dictionary per destination rank, the way the pages describe
-the transfer (FlashInfer ``NVLinkTwoSidedAlltoAll.dispatch``: send each
-token to the ranks owning its selected experts; ``NVLinkOneSidedConfig``,
-lamport paragraph: a row from rank src for its token t lands at
-src * tokens_per_rank + t).  The C oracle is written as a pull over
-destination slots; the two share nothing.  Number conversions use torch.
+the transfer (FlashInfer ``NVLinkTwoSidedAlltoAll.dispatch``: a token is
+delivered to every rank holding one of its chosen experts;
+``NVLinkOneSidedConfig``, lamport paragraph: token t of rank src occupies
+slot src * tokens_per_rank + t of a receiving rank).  The C oracle is
+written as a pull over destination slots; the two share nothing.  Number
+conversions use torch.
 """
 from __future__ import annotations
 

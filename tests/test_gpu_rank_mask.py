@@ -1,5 +1,5 @@
 """GPU parity of the active rank mask (FlashInfer moe_a2a_dispatch,
-active_rank_mask: tokens routed to a masked-off rank are dropped).  With
+active_rank_mask: a token bound for a rank whose bit is clear never reaches it).  With
 every virtual rank in one call, a masked-off rank neither sends nor
 receives: its workspace region must stay byte-for-byte untouched, live
 regions must match the oracle run with the same mask bit for bit, and the

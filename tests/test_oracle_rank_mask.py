@@ -1,5 +1,5 @@
 """Oracle pins of the active rank mask (FlashInfer moe_a2a_dispatch,
-active_rank_mask: tokens routed to a masked-off rank are dropped): the
+active_rank_mask: a token bound for a rank whose bit is clear never reaches it): the
 push-style brute force with an alive set, and invariants -- an all-ones
 mask changes nothing, dead destinations are left untouched, dead sources
 send nothing, combine sums live ranks only."""
