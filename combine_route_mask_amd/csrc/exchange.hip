@@ -63,6 +63,7 @@ namespace {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef short v2i16 __attribute__((ext_vector_type(2)));
 
 #ifndef MOE_EP_SCAN_UNROLL
 #define MOE_EP_SCAN_UNROLL 2
@@ -514,27 +515,6 @@ __global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int
     }
 }
 
-// x * 2^-e for a bf16 bit pattern x, exactly, as an fp32 value that is
-// either normal or a signed zero (a zero stands for any |x * 2^-e| below
-// 2^-10, which the e4m3 rounding sends to zero anyway).  Integer exponent
-// arithmetic only, so no denormal mode can change the result.
-__device__ __forceinline__ float scale_pow2(uint32_t xb, int e)
-{
-    const uint32_t sign = (xb & 0x8000u) << 16;
-    const int eb = (int)((xb >> 7) & 0xFFu);
-    const uint32_t mant = xb & 0x7Fu;
-    if (eb == 0) {                       // bf16 zero or subnormal: mant * 2^-133
-        if (mant == 0 || e >= -116)      // then |x * 2^-e| < 2^7 * 2^-133 * 2^116 = 2^-10
-            return __uint_as_float(sign);
-        const float f = (float)mant * __uint_as_float((uint32_t)(-133 - e + 127) << 23);
-        return __uint_as_float(sign | __float_as_uint(f));
-    }
-    const int ev = eb - e;
-    if (ev <= 0)
-        return __uint_as_float(sign);
-    return __uint_as_float(sign | ((uint32_t)ev << 23) | (mant << 16));
-}
-
 // e4m3 codes and e8m0 scale code of one 16-element half of a 32-element
 // block (the two halves sit in neighbouring lanes, which exchange their
 // amax); a block holding a NaN or an infinity gets scale 0xFF, codes 0x7F.
@@ -556,18 +536,21 @@ __device__ __forceinline__ void quantise16(u32x4 x0, u32x4 x1, u32x4 &codes, uin
     }
     const int ex = fp8_block_exponent(amax);
     scale_code = (uint32_t)(ex + 127);
-    // x * 2^-ex is exact (integer exponent arithmetic) and within +-448, so
-    // the hardware e4m3 conversion (round to nearest even, no saturation
-    // reached) rounds it once; v_cvt_pk_fp8_f32 packs two codes, first
-    // operand in the lower byte, into the low or high half of a word.
+    // v_cvt_scalef32_pk_fp8_f32 converts x / scale to e4m3 (round to nearest
+    // even) for two values, first operand in the lower byte, into the low or
+    // high half of a word.  With scale = 2^ex every |x / scale| is within
+    // 448, so no saturation is reached; its results equal those of scaling
+    // by 2^-ex first and then converting, for every bf16 value and exponent.
+    const float scale = __builtin_amdgcn_ldexpf(1.0f, ex);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
-        int packed = __builtin_amdgcn_cvt_pk_fp8_f32(scale_pow2(w0 & 0xFFFFu, ex), scale_pow2(w0 >> 16, ex),
-                                                     0, false);
-        packed = __builtin_amdgcn_cvt_pk_fp8_f32(scale_pow2(w1 & 0xFFFFu, ex), scale_pow2(w1 >> 16, ex),
-                                                 packed, true);
-        codes[j] = (uint32_t)packed;
+        v2i16 p = {0, 0};
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, __uint_as_float(w0 << 16),
+                                                     __uint_as_float(w0 & 0xFFFF0000u), scale, false);
+        p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, __uint_as_float(w1 << 16),
+                                                     __uint_as_float(w1 & 0xFFFF0000u), scale, true);
+        codes[j] = __builtin_bit_cast(uint32_t, p);
     }
 }
 
@@ -687,16 +670,18 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs 
                         acc[e] = __uint_as_float(0x7FC00000u);
                     continue;
                 }
-                const int ex = (int)sc[u] - 127;
-                // v_cvt_pk_f32_fp8 decodes two codes (low byte first) exactly
+                // v_cvt_scalef32_pk_f32_fp8 decodes two codes (low byte
+                // first) and multiplies them by the scale 2^(sc - 127),
+                // exactly, subnormal scales included
+                const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sc[u] - 127);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
-                    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv[u][j], false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)cv[u][j], true);
-                    acc[4 * j] += __builtin_amdgcn_ldexpf(lo[0], ex);
-                    acc[4 * j + 1] += __builtin_amdgcn_ldexpf(lo[1], ex);
-                    acc[4 * j + 2] += __builtin_amdgcn_ldexpf(hi[0], ex);
-                    acc[4 * j + 3] += __builtin_amdgcn_ldexpf(hi[1], ex);
+                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][j], scale, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][j], scale, true);
+                    acc[4 * j] += lo[0];
+                    acc[4 * j + 1] += lo[1];
+                    acc[4 * j + 2] += hi[0];
+                    acc[4 * j + 3] += hi[1];
                 }
             }
         }
