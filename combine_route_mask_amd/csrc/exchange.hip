@@ -34,8 +34,10 @@
 #ifndef MOE_EP_DISPATCH_LONG_ROW
 #define MOE_EP_DISPATCH_LONG_ROW 8192
 #endif
-#ifndef MOE_EP_DISPATCH_NT_LOAD
-#define MOE_EP_DISPATCH_NT_LOAD 0 // dispatch reads each token row once
+// Dispatches of at most this many (token, row chunk) items, eight rounds of
+// resident workgroups, load each row before its token's mask.
+#ifndef MOE_EP_PREFETCH_ITEMS
+#define MOE_EP_PREFETCH_ITEMS 16384
 #endif
 #ifndef MOE_EP_SCATTER_GRID
 #define MOE_EP_SCATTER_GRID 131072 // most payload-scatter workgroups of a dispatch launch
@@ -355,17 +357,23 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
 
 // Chunk c of token q's payload row (DV 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
-// chunk 0 also carries the scale row and the extra payload bytes.
-template <int KQ, int DV>
+// chunk 0 also carries the scale row and the extra payload bytes.  PF: the
+// row loads go out before the id loads of the mask, so the two latencies
+// overlap (a row whose token goes nowhere is then read for nothing); that
+// pays in steps of few workgroups and costs in large ones.
+template <int KQ, int DV, bool PF>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
     const int t = (int)(q - (int64_t)s * a.T);
     if (t >= a.n[s])
         return;
-    const uint64_t mask = route_mask<KQ>(a, q);
-    if (!mask)
-        return;
+    uint64_t mask = 0;
+    if (!PF) {
+        mask = route_mask<KQ>(a, q);
+        if (!mask)
+            return;
+    }
     const int64_t nvec = a.row_bytes >> 4;
     const int64_t i0 = c * (kBlock * DV) + threadIdx.x;
     const uint8_t *src = a.payload + q * a.row_bytes;
@@ -374,11 +382,12 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 #pragma unroll
     for (int u = 0; u < DV; ++u)
         if (i0 + u * kBlock < nvec)
-#if MOE_EP_DISPATCH_NT_LOAD
-            v[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16));
-#else
             v[u] = *reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16);
-#endif
+    if (PF) {
+        mask = route_mask<KQ>(a, q);
+        if (!mask)
+            return;
+    }
     uint64_t m = mask;
     while (m) {
         const int r = __builtin_ctzll(m);
@@ -403,8 +412,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 //   [P + plane_blocks, grid)  payload scatter, (token, row chunk) items
 // The last two roles loop over their items when there are more items than
 // blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
-// DV: 16-byte vectors per thread in a payload row chunk.
-template <int KQ, int DV>
+// DV: 16-byte vectors per thread in a payload row chunk; PF: row loads
+// before the mask (scatter_chunk).
+template <int KQ, int DV, bool PF>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
 {
@@ -425,7 +435,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     const int64_t first = a.P + plane_blocks;
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
-        scatter_chunk<KQ, DV>(a, w / nchunk, w % nchunk);
+        scatter_chunk<KQ, DV, PF>(a, w / nchunk, w % nchunk);
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
@@ -720,12 +730,20 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     const int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
     const int64_t grid =
         a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
-    if (long_rows)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG>), dim3((unsigned)grid),
-                           dim3(kBlock), 0, s, a, nplane, plane_blocks, nchunk);
+    const bool pf = S * nchunk <= MOE_EP_PREFETCH_ITEMS;
+    const dim3 g((unsigned)grid), b(kBlock);
+    if (long_rows && pf)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG, true>), g, b, 0, s, a, nplane,
+                           plane_blocks, nchunk);
+    else if (long_rows)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG, false>), g, b, 0, s, a, nplane,
+                           plane_blocks, nchunk);
+    else if (pf)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT, true>), g, b, 0, s, a, nplane,
+                           plane_blocks, nchunk);
     else
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT>), dim3((unsigned)grid),
-                           dim3(kBlock), 0, s, a, nplane, plane_blocks, nchunk);
+        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT, false>), g, b, 0, s, a, nplane,
+                           plane_blocks, nchunk);
     return hipGetLastError();
 }
 
