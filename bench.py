@@ -395,6 +395,50 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
             "combine_ms": comb_ms, "wall_s": wall}
 
 
+def trace_summary(trace_csv: str, workloads: list) -> str:
+    """Markdown table of per-launch exchange-kernel durations from a
+    rocprofv3 kernel-trace CSV of a bench run, grouped by workload (a new
+    workload starts at the first random-input kernel after exchange
+    kernels have run), kernel instance and grid.  A launch that follows a
+    1 GiB cache flush counts as cold; the first launch of an instance in a
+    workload is left out (warm-up)."""
+    import collections
+    import csv
+    import re
+    import statistics
+    ours = ("dispatch_kernel", "combine_bf16_kernel", "combine_fp8_quant_kernel",
+            "combine_fp8_gather_kernel", "allgatherv_kernel", "reduce_scatterv_kernel")
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    phase, ran, after_flush, seen = 0, False, False, set()
+    groups = collections.defaultdict(list)
+    for r in rows:
+        name = r["Kernel_Name"]
+        if "normal_kernel" in name and ran:
+            phase, ran = phase + 1, False
+            continue
+        if "FillFunctor<unsigned char>" in name and int(r["Grid_Size_X"]) >= (1 << 26):
+            after_flush = True
+            continue
+        m = re.search(r"(\w+_kernel(<[^(]*>)?)\(", name)
+        if not m or m.group(1).split("<")[0] not in ours:
+            continue
+        ran = True
+        inst, cold, after_flush = m.group(1), after_flush, False
+        if (phase, inst) not in seen:
+            seen.add((phase, inst))
+            continue
+        wg = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups[(phase, inst, wg, "cold" if cold else "warm")].append(dur)
+    out = ["| workload | kernel | workgroups | cache | launches | mean us | median us | min us |",
+           "|---|---|---|---|---|---|---|---|"]
+    for (ph, inst, wg, c), d in sorted(groups.items()):
+        label = workloads[ph] if ph < len(workloads) else str(ph)
+        out.append(f"| {label} | `{inst}` | {wg} | {c} | {len(d)} | {statistics.mean(d):.1f} | "
+                   f"{statistics.median(d):.1f} | {min(d):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def calibrate(nbytes=2 << 30, iters=10):
     """Achievable HBM bandwidth on this GPU: a plain device copy (read +
     write, torch copy_) and a fill (write only) of nbytes."""
@@ -481,6 +525,21 @@ def cpu_baseline(w, budget_s=12.0):
                      "usable_cpus": len(os.sched_getaffinity(0))}}
 
 
+def also_plan(args) -> dict:
+    """Workloads of --also in first-mention order, each with the cache
+    states (False warm, True cold) to run on its one set of buffers; the
+    primary workload in its own state is left out."""
+    plan = {}
+    for name in [a for a in args.also.split(",") if a]:
+        cold = args.cold or name.endswith("-cold")
+        base = name[:-5] if name.endswith("-cold") else name
+        if base == args.config and cold == args.cold:
+            continue
+        if cold not in plan.setdefault(base, []):
+            plan[base].append(cold)
+    return plan
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -495,9 +554,18 @@ def main():
     ap.add_argument("--cold", action="store_true", help="flush the last-level cache between steps")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="print the per-workload kernel-duration table of a rocprofv3 kernel trace "
+                         "of this bench (same --config / --also) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the counter traffic summary under profiles/ and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        labels = [args.config + ("-cold" if args.cold else "")]
+        for base, colds in also_plan(args).items():
+            labels.append(base if False in colds else base + "-cold")
+        print(trace_summary(args.trace_summary, labels), end="")
+        return
     if args.pmc_summary:
         for l in pmc_summary(*args.pmc_summary, TRAFFIC_SUMMARY, WORKLOADS[args.config].name):
             print(l)
@@ -540,16 +608,8 @@ def main():
 
     # the other workloads; warm and cold runs of one workload share its
     # buffers, so the two differ only in what the cache holds
-    plan = {}
-    for name in [a for a in args.also.split(",") if a]:
-        cold = args.cold or name.endswith("-cold")
-        base = name[:-5] if name.endswith("-cold") else name
-        if base == args.config and cold == args.cold:
-            continue
-        if cold not in plan.setdefault(base, []):
-            plan[base].append(cold)
     also = []
-    for base, colds in plan.items():
+    for base, colds in also_plan(args).items():
         wa = WORKLOADS[base]
         print(f"[bench] setting up {wa.name}", file=sys.stderr, flush=True)
         sa = AgRsSetup(wa) if base == "agrs" else Setup(wa)
