@@ -203,3 +203,40 @@ def test_dispatch_rejects_bad_steps():
     with pytest.raises(moe_ep.MoeEpError) as e:
         moe_ep.moe_ep_combine(ex.handle, pl, pl)
     assert e.value.code == moe_ep.ERR_BAD_STATE
+
+
+def test_two_handles_on_two_streams():
+    """Two exchanges with their own workspaces run concurrently on two side
+    streams (one passed explicitly, one taken from the current stream);
+    both match the oracle."""
+    from combine_route_mask_amd.moe_ep import MoeEpExchange
+    ws = [dataclasses.replace(W.EP8_BF16, name="stream a", T=48, H=1024, n_lo=0, n_hi=48),
+          dataclasses.replace(W.TINY, name="stream b", P=6, E=24, k=5, T=33, H=520, n_lo=0, n_hi=33)]
+    cases = [random_byte_case(w, 31 + i, oob=True, dup=True) for i, w in enumerate(ws)]
+    log("two handles on two side streams")
+    exs = [_exchange(w) for w in ws]
+    ins = [gpu_inputs(c) for c in cases]
+    eos = [W.draw_expert_output(w.P, w.T, w.H, 31 + i, device="cuda") for i, w in enumerate(ws)]
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    cur = torch.cuda.current_stream()
+    outs, ys = [], []
+    for i, (w, c, ex, (pl, sc, ids, wt), eo, st) in enumerate(zip(ws, cases, exs, ins, eos, streams)):
+        st.wait_stream(cur)
+        with torch.cuda.stream(st):
+            if i == 0:
+                outs.append(ex.dispatch(pl, ids, wt, scales=sc, num_tokens=c.counts.tolist(),
+                                        runtime_max_tokens_per_rank=w.T, stream=st))
+                ys.append(ex.combine(eo, stream=st))
+            else:
+                outs.append(ex.dispatch(pl, ids, wt, scales=sc, num_tokens=c.counts.tolist(),
+                                        runtime_max_tokens_per_rank=w.T))
+                ys.append(ex.combine(eo))
+    torch.cuda.synchronize()
+    for c, out in zip(cases, outs):
+        _check(c, out)
+    for w, c, eo, y in zip(ws, cases, eos, ys):
+        ref, _ = oracle.combine_bf16(c.counts, c.ids, eo.view(torch.int16).cpu().numpy().view(np.uint16), E=w.E)
+        yv = y.float().cpu().numpy().astype(np.float64)
+        for s in range(w.P):
+            n = int(c.counts[s])
+            assert np.all(np.abs(yv[s, :n] - ref[s, :n]) <= 2.0 ** -7 * np.abs(ref[s, :n]) + 1e-3)
