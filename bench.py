@@ -37,7 +37,10 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
-TRAFFIC_SUMMARY = os.path.join(ROOT, "profiles", "pmc_traffic_ep8_bf16.txt")
+def traffic_summary_path(config: str) -> str:
+    """Committed counter summary of a bench workload (profiles/)."""
+    name = "ep8_bf16" if config == "ep8" else config.replace("-", "_")
+    return os.path.join(ROOT, "profiles", f"pmc_traffic_{name}.txt")
 KERNEL_SOURCE = os.path.join(ROOT, "combine_route_mask_amd", "csrc", "exchange.hip")
 
 
@@ -46,12 +49,12 @@ def source_digest() -> str:
     return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str):
+def measured_traffic(kernel: str, workload: str, config: str):
     """HBM bytes per launch of `kernel` on `workload` from the committed
     counter summary, or None when there is none or the kernel source has
     changed since the counters were taken."""
     try:
-        rows = [json.loads(l) for l in open(TRAFFIC_SUMMARY) if l.startswith("{")]
+        rows = [json.loads(l) for l in open(traffic_summary_path(config)) if l.startswith("{")]
     except OSError:
         return None
     for r in rows:
@@ -61,7 +64,7 @@ def measured_traffic(kernel: str, workload: str):
     return None
 
 
-def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str):
+def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, config: str = "ep8"):
     """Per-launch HBM traffic from two counter runs (FETCH_SIZE, WRITE_SIZE;
     KiB per dispatch).  Each counter is scaled by what it reads for the
     calibration copy kernel of known size (2 GiB read + 2 GiB written)."""
@@ -94,16 +97,18 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str):
             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
             "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
             "launches": len(vs), "source_digest": source_digest()}))
+    cfg = "" if config == "ep8" else f" --config {config}"
+    run = f"python3 <repo>/bench.py{cfg} --also '' --no-cpu-baseline --no-graph --steps {6 if config == 'ep8' else 3} --warmup 2"
     with open(out_path, "w") as f:
         f.write("# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE in KiB per\n"
                 "# dispatch), each scaled by its reading for a plain 2 GiB device copy\n"
                 "# (calibration copy in bench.py: 2 GiB read, 2 GiB written).  Commands, run from /tmp\n"
                 "# with TMPDIR=/tmp (<repo>: this repository, <out>: any output directory):\n"
                 "#   rocprofv3 --pmc FETCH_SIZE -d <out>/pmc_fetch -o pmc --output-format csv -- \\\n"
-                "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
+                f"#       {run}\n"
                 "#   rocprofv3 --pmc WRITE_SIZE -d <out>/pmc_write -o pmc --output-format csv -- \\\n"
-                "#       python3 <repo>/bench.py --also '' --no-cpu-baseline --no-graph --steps 6 --warmup 2\n"
-                "#   python3 <repo>/bench.py --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
+                f"#       {run}\n"
+                f"#   python3 <repo>/bench.py{cfg} --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
                 "#       <out>/pmc_write/pmc_counter_collection.csv\n"
                 "# source_digest: first 16 hex digits of sha256(combine_route_mask_amd/csrc/exchange.hip)\n")
         for l in lines:
@@ -567,7 +572,8 @@ def main():
         print(trace_summary(args.trace_summary, labels), end="")
         return
     if args.pmc_summary:
-        for l in pmc_summary(*args.pmc_summary, TRAFFIC_SUMMARY, WORKLOADS[args.config].name):
+        for l in pmc_summary(*args.pmc_summary, traffic_summary_path(args.config),
+                             WORKLOADS[args.config].name, args.config):
             print(l)
         return
     if args.gpus != 1:
@@ -600,7 +606,7 @@ def main():
         dom_name, dom_ms, dom_bytes = ("dispatch_kernel", m["dispatch_ms"], b["dispatch"]) \
             if m["dispatch_ms"] >= m["combine_ms"] else ("combine_bf16_kernel", m["combine_ms"], b["combine"])
     achieved = dom_bytes / (dom_ms / 1e3) / 1e9
-    traffic = measured_traffic(dom_name, w.name)
+    traffic = measured_traffic(dom_name, w.name, args.config)
     roofline = {"bound": "hbm", "kernel": dom_name, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                 "bytes_per_launch": dom_bytes, "launch_ms": dom_ms,
