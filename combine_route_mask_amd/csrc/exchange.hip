@@ -66,6 +66,7 @@ namespace {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short v2i16 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef MOE_EP_SCAN_UNROLL
 #define MOE_EP_SCAN_UNROLL 2
@@ -525,23 +526,24 @@ __global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int
     }
 }
 
-// e4m3 codes and e8m0 scale code of one 16-element half of a 32-element
-// block (the two halves sit in neighbouring lanes, which exchange their
-// amax); a block holding a NaN or an infinity gets scale 0xFF, codes 0x7F.
-// All lanes of the wave must call this together (lane shuffle).
-__device__ __forceinline__ void quantise16(u32x4 x0, u32x4 x1, u32x4 &codes, uint32_t &scale_code)
+// e4m3 codes (two words, element 0 in the lowest byte) and e8m0 scale code
+// of one 8-element quarter of a 32-element block; the block's four quarters
+// sit in four consecutive lanes (lane & ~3 .. lane | 3), which exchange
+// their amax.  A block holding a NaN or an infinity gets scale 0xFF and
+// codes 0x7F.  All lanes of the wave must call this together (shuffles).
+__device__ __forceinline__ void quantise8(u32x4 x, uint32_t &c0, uint32_t &c1, uint32_t &scale_code)
 {
-    const uint32_t w[8] = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
     uint32_t amax = 0;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        amax = max(amax, w[e] & 0x7FFFu);
-        amax = max(amax, (w[e] >> 16) & 0x7FFFu);
+    for (int e = 0; e < 4; ++e) {
+        amax = max(amax, x[e] & 0x7FFFu);
+        amax = max(amax, (x[e] >> 16) & 0x7FFFu);
     }
     amax = max(amax, (uint32_t)__shfl_xor((int)amax, 1));
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 2));
     if (amax >= 0x7F80u) {
         scale_code = 0xFFu;
-        codes = u32x4{0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu};
+        c0 = c1 = 0x7F7F7F7Fu;
         return;
     }
     const int ex = fp8_block_exponent(amax);
@@ -552,40 +554,49 @@ __device__ __forceinline__ void quantise16(u32x4 x0, u32x4 x1, u32x4 &codes, uin
     // 448, so no saturation is reached; its results equal those of scaling
     // by 2^-ex first and then converting, for every bf16 value and exponent.
     const float scale = __builtin_amdgcn_ldexpf(1.0f, ex);
+    uint32_t c[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t w0 = w[2 * j], w1 = w[2 * j + 1];
+    for (int j = 0; j < 2; ++j) {
+        const uint32_t w0 = x[2 * j], w1 = x[2 * j + 1];
         v2i16 p = {0, 0};
         p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, __uint_as_float(w0 << 16),
                                                      __uint_as_float(w0 & 0xFFFF0000u), scale, false);
         p = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(p, __uint_as_float(w1 << 16),
                                                      __uint_as_float(w1 & 0xFFFF0000u), scale, true);
-        codes[j] = __builtin_bit_cast(uint32_t, p);
+        c[j] = __builtin_bit_cast(uint32_t, p);
     }
+    c0 = c[0];
+    c1 = c[1];
 }
 
-// FP8 combine, sending side: item (token q = s*T + t, chunk c of 256
-// 16-element groups).  Every rank r that holds the token quantises its row
-// q (e4m3fn, one e8m0 scale per 32 elements) into source rank s's landing
-// plane at slot r*T + t; the rows of up to G ranks are loaded before any is
-// quantised.  Each lane owns one 16-element group; lane pairs share a block.
+// FP8 combine, sending side: item (token q = s*T + t, chunk c of 4096
+// elements).  Every rank r that holds the token quantises its row q (e4m3fn,
+// one e8m0 scale per 32 elements) into source rank s's landing plane at slot
+// r*T + t; the rows of up to G ranks are loaded before any is quantised.
+// Each lane owns 8 elements in each half of the chunk (elements
+// c*4096 + h*2048 + lane*8 ..), so every load instruction of a wave covers
+// 1 KB of a row without gaps; four lanes share a block.
 template <int G>
 __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t rank_bytes = S * a.H * 2;
-    const int64_t ngroups = a.H >> 4;
     for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
         const int64_t q = w / nchunk, c = w % nchunk;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
         if (t >= a.n[s])
             continue;
-        const int64_t g = c * kBlock + threadIdx.x;
-        const bool act = g < ngroups; // ngroups and kBlock even: lane pairs agree
+        int64_t e[2];
+        bool act[2]; // H % 32 == 0: the four lanes of a block agree
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
+            act[h] = e[h] < a.H;
+        }
         uint8_t *land = a.ws + (int64_t)s * a.region;
         const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2 + g * 32;
+        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2;
         uint64_t m = mask;
         while (m) {
             int r[G];
@@ -604,21 +615,22 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a
             for (int u = 0; u < G; ++u)
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
-                    x[u][h] = (act && u < cnt)
-                                  ? load16_nt(src + (int64_t)r[u] * rank_bytes + h * 16)
-                                  : u32x4{0u, 0u, 0u, 0u};
+                    x[u][h] = (act[h] && u < cnt) ? load16_nt(src + (int64_t)r[u] * rank_bytes + e[h] * 2)
+                                                  : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 if (u >= cnt)
                     break;
-                u32x4 codes;
-                uint32_t sc;
-                quantise16(x[u][0], x[u][1], codes, sc);
-                if (act) {
-                    const int64_t slot = (int64_t)r[u] * a.T + t;
-                    *reinterpret_cast<u32x4 *>(land + a.off_land_codes + slot * a.H + g * 16) = codes;
-                    if ((g & 1) == 0)
-                        land[a.off_land_scales + slot * (a.H >> 5) + (g >> 1)] = (uint8_t)sc;
+                const int64_t slot = (int64_t)r[u] * a.T + t;
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    uint32_t c0, c1, sc;
+                    quantise8(x[u][h], c0, c1, sc);
+                    if (act[h]) {
+                        *reinterpret_cast<u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]) = u32x2{c0, c1};
+                        if ((threadIdx.x & 3) == 0)
+                            land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)] = (uint8_t)sc;
+                    }
                 }
             }
         }
