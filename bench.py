@@ -41,12 +41,17 @@ def traffic_summary_path(config: str) -> str:
     """Committed counter summary of a bench workload (profiles/)."""
     name = "ep8_bf16" if config == "ep8" else config.replace("-", "_")
     return os.path.join(ROOT, "profiles", f"pmc_traffic_{name}.txt")
-KERNEL_SOURCE = os.path.join(ROOT, "combine_route_mask_amd", "csrc", "exchange.hip")
+# device sources of the kernels the counter summaries describe
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f)
+                  for f in ("exchange.hip", "agrs.hip", "formats.h", "moe_ep_internal.h")]
 
 
 def source_digest() -> str:
     import hashlib
-    return hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        h.update(open(path, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel: str, workload: str, config: str):
@@ -86,8 +91,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
     f_scale = copy_kib / (sum(cf) / len(cf))
     w_scale = copy_kib / (sum(cw) / len(cw))
     lines = []
+    family = ("allgatherv_kernel", "reduce_scatterv_kernel") if config == "agrs" else \
+        ("dispatch_kernel", "combine_")
     for (k, g), vs in sorted(fetch.items()):
-        if "moe_ep" not in k and not k.startswith(("dispatch_kernel", "combine_")):
+        if not k.startswith(family):
             continue
         wv = write.get((k, g), [0.0])
         fk, wk = sum(vs) / len(vs), sum(wv) / len(wv)
@@ -98,7 +105,11 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
             "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
             "launches": len(vs), "source_digest": source_digest()}))
     cfg = "" if config == "ep8" else f" --config {config}"
-    run = f"python3 <repo>/bench.py{cfg} --also '' --no-cpu-baseline --no-graph --steps {6 if config == 'ep8' else 3} --warmup 2"
+    if config == "agrs":  # the AgRs step runs as an extra workload of the default bench
+        run = "python3 <repo>/bench.py --also agrs --no-cpu-baseline --no-graph --steps 3 --warmup 2"
+    else:
+        run = (f"python3 <repo>/bench.py{cfg} --also '' --no-cpu-baseline --no-graph "
+               f"--steps {6 if config == 'ep8' else 3} --warmup 2")
     with open(out_path, "w") as f:
         f.write("# HBM traffic per launch from rocprofv3 counters (FETCH_SIZE, WRITE_SIZE in KiB per\n"
                 "# dispatch), each scaled by its reading for a plain 2 GiB device copy\n"
@@ -110,7 +121,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
                 f"#       {run}\n"
                 f"#   python3 <repo>/bench.py{cfg} --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
                 "#       <out>/pmc_write/pmc_counter_collection.csv\n"
-                "# source_digest: first 16 hex digits of sha256(combine_route_mask_amd/csrc/exchange.hip)\n")
+                "# source_digest: first 16 hex digits of the sha256 of combine_route_mask_amd/csrc/\n"
+                "# exchange.hip, agrs.hip, formats.h and moe_ep_internal.h, concatenated\n")
         for l in lines:
             f.write(l + "\n")
     return lines
