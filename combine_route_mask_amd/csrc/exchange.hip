@@ -358,7 +358,8 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
 
 // Chunk c of token q's payload row (DV 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
-// chunk 0 also carries the scale row and the extra payload bytes.  PF: the
+// chunk 0 also carries the scale row (loaded with the payload vectors when it
+// is at most 256 aligned 16-byte words) and the extra payload bytes.  PF: the
 // row loads go out before the id loads of the mask, so the two latencies
 // overlap (a row whose token goes nowhere is then read for nothing); that
 // pays in steps of few workgroups and costs in large ones.
@@ -384,6 +385,14 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
     for (int u = 0; u < DV; ++u)
         if (i0 + u * kBlock < nvec)
             v[u] = *reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16);
+    // a scale row of at most 256 16-byte words travels with chunk 0's loads
+    const bool sc_vec = c == 0 && a.srow_bytes && (a.srow_bytes >> 4) <= kBlock &&
+                        (((uint64_t)(uintptr_t)a.scales | (uint64_t)a.srow_bytes | (uint64_t)a.off_scales |
+                          (uint64_t)a.region) & 15) == 0;
+    const bool sc_lane = sc_vec && (int64_t)threadIdx.x < (a.srow_bytes >> 4);
+    u32x4 sv = {0u, 0u, 0u, 0u};
+    if (sc_lane)
+        sv = *reinterpret_cast<const u32x4 *>(a.scales + q * a.srow_bytes + threadIdx.x * 16);
     if (PF) {
         mask = route_mask<KQ>(a, q);
         if (!mask)
@@ -398,8 +407,10 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
         for (int u = 0; u < DV; ++u)
             if (i0 + u * kBlock < nvec)
                 store16(d + (i0 + u * kBlock) * 16, v[u]);
+        if (sc_lane)
+            store16(a.ws + a.off_scales + (int64_t)r * a.region + q * a.srow_bytes + threadIdx.x * 16, sv);
     }
-    if (c == 0 && a.srow_bytes)
+    if (c == 0 && a.srow_bytes && !sc_vec)
         copy_row_any(a.scales + q * a.srow_bytes, a.srow_bytes, mask,
                      a.ws + a.off_scales + q * a.srow_bytes, a.region);
     if (c == 0 && a.xrow_bytes)
