@@ -648,28 +648,37 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a
     }
 }
 
-// FP8 combine, receiving side: item (token q = s*T + t, chunk c of 256
-// 16-element groups).  Each lane dequantises its group of the landing rows
-// r*T + t of every rank r in the token's mask (codes of up to G ranks loaded
-// at once), sums them in fp32 in ascending rank order and rounds to bf16.
+// FP8 combine, receiving side: item (token q = s*T + t, chunk c of 4096
+// elements, the quantising side's lane layout).  Each lane dequantises its
+// 8 elements in each half of the chunk from the landing rows r*T + t of every
+// rank r in the token's mask (codes of up to G ranks loaded at once), sums
+// them in fp32 in ascending rank order, rounds to bf16 and stores the output
+// non-temporally (it is not read again in the step).
 template <int G>
 __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
-    const int64_t ngroups = a.H >> 4;
     for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
         const int64_t q = w / nchunk, c = w % nchunk;
         const int s = (int)(q / a.T);
         const int t = (int)(q - (int64_t)s * a.T);
-        const int64_t g = c * kBlock + threadIdx.x;
-        if (t >= a.n[s] || g >= ngroups)
+        int64_t e[2];
+        bool act[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
+            act[h] = e[h] < a.H;
+        }
+        if (t >= a.n[s] || !act[0])
             continue;
         const uint8_t *land = a.ws + (int64_t)s * a.region;
         const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
-        float acc[16];
+        float acc[2][8];
 #pragma unroll
-        for (int e = 0; e < 16; ++e)
-            acc[e] = 0.0f;
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                acc[h][j] = 0.0f;
         uint64_t m = mask;
         while (m) {
             int r[G];
@@ -683,50 +692,63 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs 
                     cnt = u + 1;
                 }
             }
-            u32x4 cv[G];
-            uint32_t sc[G];
+            u32x2 cv[G][2];
+            uint32_t sc[G][2];
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 if (u < cnt) {
                     const int64_t slot = (int64_t)r[u] * a.T + t;
-                    cv[u] = load16_nt(land + a.off_land_codes + slot * a.H + g * 16);
-                    sc[u] = land[a.off_land_scales + slot * (a.H >> 5) + (g >> 1)];
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        if (act[h]) {
+                            cv[u][h] = __builtin_nontemporal_load(
+                                reinterpret_cast<const u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]));
+                            sc[u][h] = land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)];
+                        }
+                    }
                 }
             }
 #pragma unroll
             for (int u = 0; u < G; ++u) {
                 if (u >= cnt)
                     break;
-                if (sc[u] == 0xFFu) {
 #pragma unroll
-                    for (int e = 0; e < 16; ++e)
-                        acc[e] = __uint_as_float(0x7FC00000u);
-                    continue;
-                }
-                // v_cvt_scalef32_pk_f32_fp8 decodes two codes (low byte
-                // first) and multiplies them by the scale 2^(sc - 127),
-                // exactly, subnormal scales included
-                const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sc[u] - 127);
+                for (int h = 0; h < 2; ++h) {
+                    if (!act[h])
+                        continue;
+                    if (sc[u][h] == 0xFFu) {
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][j], scale, false);
-                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][j], scale, true);
-                    acc[4 * j] += lo[0];
-                    acc[4 * j + 1] += lo[1];
-                    acc[4 * j + 2] += hi[0];
-                    acc[4 * j + 3] += hi[1];
+                        for (int j = 0; j < 8; ++j)
+                            acc[h][j] = __uint_as_float(0x7FC00000u);
+                        continue;
+                    }
+                    // v_cvt_scalef32_pk_f32_fp8 decodes two codes (low byte
+                    // first) and multiplies them by the scale 2^(sc - 127),
+                    // exactly, subnormal scales included
+                    const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sc[u][h] - 127);
+#pragma unroll
+                    for (int j = 0; j < 2; ++j) {
+                        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, false);
+                        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, true);
+                        acc[h][4 * j] += lo[0];
+                        acc[h][4 * j + 1] += lo[1];
+                        acc[h][4 * j + 2] += hi[0];
+                        acc[h][4 * j + 3] += hi[1];
+                    }
                 }
             }
         }
-        u32x4 o0, o1;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            o0[j] = pack_bf16x2(acc[2 * j], acc[2 * j + 1]);
-            o1[j] = pack_bf16x2(acc[8 + 2 * j], acc[8 + 2 * j + 1]);
+        for (int h = 0; h < 2; ++h) {
+            if (!act[h])
+                continue;
+            u32x4 o;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                o[j] = pack_bf16x2(acc[h][2 * j], acc[h][2 * j + 1]);
+            u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + e[h]);
+            __builtin_nontemporal_store(o, dst);
         }
-        u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + g * 16);
-        dst[0] = o0;
-        dst[1] = o1;
     }
 }
 
