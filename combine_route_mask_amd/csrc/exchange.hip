@@ -102,8 +102,9 @@ __device__ __forceinline__ uint64_t owner_bit(const DispatchArgs &a, int id)
 
 // Destination-rank mask of token q: bit r set when one of its k ids is an
 // expert of rank r and rank r takes part in the step.  OR-ing the bits
-// deduplicates tokens with several experts on one rank.  KQ > 0: the k = 4*KQ ids are read as KQ 16-byte
-// vectors; KQ == 0: any k, all loads of the first 16 ids issued together.
+// deduplicates tokens with several experts on one rank.  KQ > 0: the
+// k = 4*KQ ids are read as KQ 16-byte vectors; KQ == 0: any k, all loads of
+// the first 16 ids issued together.
 template <int KQ>
 __device__ __forceinline__ uint64_t route_mask(const DispatchArgs &a, int64_t q)
 {
@@ -175,8 +176,9 @@ __device__ __forceinline__ void copy_row_any(const uint8_t *src, int64_t nbytes,
 
 // Receive bookkeeping of destination rank r (and, when given, the EPLB
 // statistics all-gather into its region): walks every source slot q in
-// ascending order, 1024 slots per step (four per lane, all id rows loaded
-// before any is tested); a wave ballot marks the slots whose token goes to
+// ascending order, kBlock * kScanUnroll slots per step (kScanUnroll per
+// lane, all id rows loaded before any is tested); a wave ballot marks the
+// slots whose token goes to
 // r, v_mbcnt gives each one its rank inside the wave, and the per-wave
 // totals in LDS give the step's exclusive prefix.  Produces the ascending
 // list of valid slots, the per-source counts and their exclusive prefix
