@@ -47,10 +47,16 @@ KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f)
 
 
 def source_digest() -> str:
+    """Digest of the device sources with comments and blank space removed,
+    so that editing a comment does not retire the counter summaries."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for path in KERNEL_SOURCES:
-        h.update(open(path, "rb").read())
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", "", text)
+        h.update("".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 
@@ -122,7 +128,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
                 f"#   python3 <repo>/bench.py{cfg} --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
                 "#       <out>/pmc_write/pmc_counter_collection.csv\n"
                 "# source_digest: first 16 hex digits of the sha256 of combine_route_mask_amd/csrc/\n"
-                "# exchange.hip, agrs.hip, formats.h and moe_ep_internal.h, concatenated\n")
+                "# exchange.hip, agrs.hip, formats.h and moe_ep_internal.h, concatenated, with\n"
+                "# comments and white space removed\n")
         for l in lines:
             f.write(l + "\n")
     return lines

@@ -178,9 +178,8 @@ __device__ __forceinline__ void copy_row_any(const uint8_t *src, int64_t nbytes,
 // statistics all-gather into its region): walks every source slot q in
 // ascending order, kBlock * kScanUnroll slots per step (kScanUnroll per
 // lane, all id rows loaded before any is tested); a wave ballot marks the
-// slots whose token goes to
-// r, v_mbcnt gives each one its rank inside the wave, and the per-wave
-// totals in LDS give the step's exclusive prefix.  Produces the ascending
+// slots whose token goes to r, v_mbcnt gives each one its rank inside the
+// wave, and the per-wave totals in LDS give the step's exclusive prefix.  Produces the ascending
 // list of valid slots, the per-source counts and their exclusive prefix
 // (src_offsets[P] = rows received).
 template <int KQ>
