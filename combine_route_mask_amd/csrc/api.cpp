@@ -106,7 +106,7 @@ int check_params(const moe_ep_params *pp, Layout *lay)
     if (p.dispatch_format == MOE_EP_FMT_DEEPSEEK_FP8 && p.hidden_size % 128 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG, "DeepSeekFp8 payloads need hidden_size % 128 == 0");
     if (p.extra_payload_bytes_per_token < 0)
-        return fail(MOE_EP_ERR_INVALID_ARG, "extra_payload_bytes_per_token must be non-negative");
+        return fail(MOE_EP_ERR_INVALID_ARG, "extra_payload_bytes_per_token may not be negative");
     if (p.eplb_stats_num_experts < 0)
         return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_num_experts must be non-negative");
     if (p.hidden_size % 8 != 0)

@@ -11,7 +11,7 @@
  *    delivers every token to each rank that holds one of its chosen
  *    experts, together with the token's top-k ids, top-k weights and scale
  *    row; combine() adds up, over ranks, each token's expert outputs
- *    (already weighted and reduced over a rank's local experts); destroy() is
+ *    (each rank having weighted them and summed over its own experts); destroy() is
  *    idempotent; is_platform_supported() performs no collective work.
  *  - FlashInfer "flashinfer.moe_ep.NVLinkOneSidedConfig", lamport
  *    paragraph: token t of rank src lands in slot src * tokens_per_rank + t
@@ -160,7 +160,7 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
  *                    more bytes per token, forwarded like the scale row
  *                    (NVLinkOneSidedConfig, extra_payload_bytes_per_token)
  *  eplb_local_stats  device [P][eplb_stats_num_experts] int32 or NULL: each
- *                    rank's expert-load statistics; every live rank receives
+ *                    rank's per-expert counters for load balancing; every live rank receives
  *                    the [P][n] matrix (row s = rank s's statistics) in its
  *                    region (moe_a2a_dispatch, eplb_local_stats ->
  *                    eplb_gathered_stats)

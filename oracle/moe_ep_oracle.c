@@ -23,7 +23,7 @@
  *    beyond the sending rank's token count is marked with expert id
  *    num_experts, outside every rank's range.
  *  - FlashInfer "NVLinkTwoSidedAlltoAll", combine(): each token's expert
- *    outputs, already weighted and reduced over a rank's local experts,
+ *    outputs, which each rank has weighted and summed over its own experts,
  *    summed over ranks into a [local_num_tokens, hidden] result.
  *  - FlashInfer "NVLinkOneSidedConfig", first options paragraph:
  *    with use_low_precision_combine the combine moves its rows as FP8
