@@ -94,6 +94,13 @@ SMALL = [
                         n_lo=700, n_hi=1500),
     dataclasses.replace(W.TINY, name="k16", P=8, E=64, k=16, T=50, H=256, n_lo=0, n_hi=50),
     dataclasses.replace(W.TINY, name="k64 all experts", P=4, E=64, k=64, T=20, H=128, n_lo=0, n_hi=20),
+    dataclasses.replace(W.TINY, name="bf16 H16384 two long chunks", P=4, E=16, k=3, T=6, H=16384,
+                        n_lo=0, n_hi=6),
+    dataclasses.replace(W.EP8_MXFP8, name="mxfp8 H8192 long rows", P=4, E=32, T=7, H=8192, n_lo=2, n_hi=7),
+    dataclasses.replace(W.EP8_MXFP8, name="mxfp8 H16384 scale row 512B", P=3, E=12, k=4, T=5, H=16384,
+                        n_lo=1, n_hi=5, routing="uniform"),
+    dataclasses.replace(W.EP64_NVFP4, name="nvfp4 H4096 scale row 256B", P=8, E=32, T=9, H=4096,
+                        n_lo=0, n_hi=9),
 ]
 
 
