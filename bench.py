@@ -599,6 +599,9 @@ def main():
         print(json.dumps({"error": "this exchange runs P virtual EP ranks on one GPU; "
                                    "--gpus above 1 is not supported"}))
         sys.exit(2)
+    if args.config == "agrs":
+        print(json.dumps({"error": "the AgRs step runs as an extra workload: --also agrs"}))
+        sys.exit(2)
 
     import torch
     from combine_route_mask_amd import moe_ep
