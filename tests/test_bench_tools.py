@@ -1,0 +1,78 @@
+"""The bench's profile post-processing on small synthetic rocprofv3 CSVs:
+the kernel-trace table (workload phases, cold launches, warm-up launch left
+out) and the counter summary (scaled by the calibration copy)."""
+import csv
+import json
+
+import bench
+
+TRACE_COLS = ["Kind", "Agent_Id", "Queue_Id", "Stream_Id", "Thread_Id", "Dispatch_Id", "Kernel_Id",
+              "Kernel_Name", "Correlation_Id", "Start_Timestamp", "End_Timestamp", "LDS_Block_Size",
+              "Scratch_Size", "VGPR_Count", "Accum_VGPR_Count", "SGPR_Count", "Workgroup_Size_X",
+              "Workgroup_Size_Y", "Workgroup_Size_Z", "Grid_Size_X", "Grid_Size_Y", "Grid_Size_Z"]
+
+DISPATCH = "void moe_ep::(anonymous namespace)::dispatch_kernel<2, 4, true>(moe_ep::DispatchArgs, long, long, long)"
+COMBINE = "void moe_ep::(anonymous namespace)::combine_bf16_kernel<1, 8, true>(moe_ep::CombineArgs, long)"
+NORMAL = "void at::native::distribution_elementwise_grid_stride_kernel<float, 4, normal_kernel>(int)"
+FLUSH = "void at::native::vectorized_elementwise_kernel<16, at::native::FillFunctor<unsigned char>, x>(int)"
+
+
+def _trace(path, kernels):
+    t = 0
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=TRACE_COLS)
+        w.writeheader()
+        for name, grid, dur in kernels:
+            row = {c: 0 for c in TRACE_COLS}
+            row.update(Kernel_Name=name, Start_Timestamp=t, End_Timestamp=t + dur,
+                       Workgroup_Size_X=256, Grid_Size_X=grid)
+            w.writerow(row)
+            t += dur + 1000
+
+
+def test_trace_summary_phases_and_cold(tmp_path):
+    p = tmp_path / "trace.csv"
+    _trace(p, [
+        (NORMAL, 2048 * 256, 500),
+        (DISPATCH, 1036 * 256, 99000),      # first launch of the phase: left out
+        (DISPATCH, 1036 * 256, 12000),
+        (DISPATCH, 1036 * 256, 14000),
+        (COMBINE, 4096 * 256, 13000),
+        (NORMAL, 2048 * 256, 500),          # second workload starts
+        (DISPATCH, 1036 * 256, 50000),      # warm-up, left out
+        (FLUSH, 1 << 26, 100000),
+        (DISPATCH, 1036 * 256, 20000),      # after a flush: cold
+        (DISPATCH, 1036 * 256, 12000),
+    ])
+    lines = bench.trace_summary(str(p), ["first", "second"]).splitlines()
+    rows = [l.split("|")[1:-1] for l in lines[2:]]
+    rows = [[c.strip() for c in r] for r in rows]
+    assert ["first", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "2", "13.0", "13.0", "12.0"] in rows
+    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "cold", "1", "20.0", "20.0", "20.0"] in rows
+    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "1", "12.0", "12.0", "12.0"] in rows
+    assert not any(r[1].startswith("`combine") and r[0] == "first" and r[4] != "1" for r in rows)
+
+
+def _pmc(path, entries):
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Value"])
+        w.writeheader()
+        for name, grid, val in entries:
+            w.writerow({"Kernel_Name": name, "Grid_Size": grid, "Counter_Value": val})
+
+
+def test_pmc_summary_scales_by_the_copy(tmp_path):
+    copy_kib = (2 << 30) / 1024
+    fetch, write, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "out.txt"
+    # the counters read half the copy's fetched bytes and all of its written bytes
+    _pmc(fetch, [("__amd_rocclr_copyBuffer", 256, copy_kib / 2), (COMBINE, 1048576, 1000.0),
+                 (COMBINE, 1048576, 1200.0)])
+    _pmc(write, [("__amd_rocclr_copyBuffer", 256, copy_kib), (COMBINE, 1048576, 300.0),
+                 (COMBINE, 1048576, 300.0)])
+    lines = bench.pmc_summary(str(fetch), str(write), str(out), "wl")
+    assert len(lines) == 1
+    r = json.loads(lines[0])
+    assert r["kernel"] == "combine_bf16_kernel" and r["fetch_scale"] == 2.0 and r["write_scale"] == 1.0
+    assert r["hbm_bytes_per_launch"] == int(round((1100.0 * 2 + 300.0) * 1024))
+    assert r["source_digest"] == bench.source_digest()
+    assert open(out).read().count("\n{") == 1
