@@ -43,7 +43,7 @@ def traffic_summary_path(config: str) -> str:
     return os.path.join(ROOT, "profiles", f"pmc_traffic_{name}.txt")
 # device sources of the kernels the counter summaries describe
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f)
-                  for f in ("exchange.hip", "agrs.hip", "formats.h", "moe_ep_internal.h")]
+                  for f in ("exchange.hip", "agrs.hip", "formats.h", "memory_ops.h", "moe_ep_internal.h")]
 
 
 def source_digest() -> str:

@@ -16,11 +16,19 @@
 #include <algorithm>
 
 #include "formats.h"
+#include "memory_ops.h"
 #include "moe_ep_internal.h"
 
 // Tuning knobs (compile-time; defaults are the measured best on MI355X).
-#ifndef MOE_EP_NT_STORE
-#define MOE_EP_NT_STORE 1     // dispatch row stores bypass the caches' retention
+// Launches whose row stores total at most this many bytes write them
+// through L2 (write-through stores); larger ones store non-temporally.  At
+// the end of a kernel every L2 writes back its dirty lines before the next
+// kernel may start, a cost of ~2 us that write-through stores avoid; per
+// byte they are slower than non-temporal ones (1-3% on long rows, ~25% on
+// rows of a few KB), so they pay only where that flush is a sizeable part of
+// the launch.
+#ifndef MOE_EP_WT_BYTES
+#define MOE_EP_WT_BYTES (256ll << 20)
 #endif
 // 16-byte vectors per thread in a dispatch row chunk, for payload rows of at
 // least MOE_EP_DISPATCH_LONG_ROW bytes and for shorter ones (short rows split
@@ -42,16 +50,16 @@
 #ifndef MOE_EP_SCATTER_GRID
 #define MOE_EP_SCATTER_GRID 131072 // most payload-scatter workgroups of a dispatch launch
 #endif
-// BF16 combine shapes: (16-byte vectors per thread, ranks loaded at once,
-// non-temporal output stores) for outputs that fit the 256 MB last-level
-// cache and for larger ones.  Output rows are not read again within a step,
-// so both store them non-temporally (which also leaves the cache to the next
-// dispatch's rows).
+// BF16 combine shapes: (16-byte vectors per thread, ranks loaded at once)
+// for outputs below MOE_EP_COMBINE_LARGE_BYTES and for larger ones.  Output
+// rows are not read again within a step, so they never stay in the caches:
+// written through for outputs of at most MOE_EP_WT_BYTES, non-temporal
+// above.
 #ifndef MOE_EP_COMBINE_SMALL
-#define MOE_EP_COMBINE_SMALL 1, 8, 1
+#define MOE_EP_COMBINE_SMALL 1, 8
 #endif
 #ifndef MOE_EP_COMBINE_LARGE
-#define MOE_EP_COMBINE_LARGE 4, 2, 1
+#define MOE_EP_COMBINE_LARGE 4, 2
 #endif
 #ifndef MOE_EP_FP8_GATHER
 #define MOE_EP_FP8_GATHER 2 // ranks per round in the FP8 combine kernels
@@ -63,10 +71,8 @@
 namespace moe_ep {
 namespace {
 
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef short v2i16 __attribute__((ext_vector_type(2)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 
 #ifndef MOE_EP_SCAN_UNROLL
 #define MOE_EP_SCAN_UNROLL 2
@@ -76,18 +82,14 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
 constexpr int kPlaneGroup = 8;          // destinations per id-plane item
 
-__device__ __forceinline__ u32x4 load16_nt(const void *p)
+// A 16-byte row store: write-through (WT) or non-temporal.
+template <bool WT>
+__device__ __forceinline__ void store_row16(void *p, u32x4 v)
 {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
-}
-
-__device__ __forceinline__ void store16(void *p, u32x4 v)
-{
-#if MOE_EP_NT_STORE
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
-#else
-    *reinterpret_cast<u32x4 *>(p) = v;
-#endif
+    if constexpr (WT)
+        store16_wt(p, v);
+    else
+        __builtin_nontemporal_store(v, reinterpret_cast<u32x4 *>(p));
 }
 
 // Bit of the rank owning expert id (experts are owned in contiguous blocks
@@ -364,7 +366,7 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
 // row loads go out before the id loads of the mask, so the two latencies
 // overlap (a row whose token goes nowhere is then read for nothing); that
 // pays in steps of few workgroups and costs in large ones.
-template <int KQ, int DV, bool PF>
+template <int KQ, int DV, bool PF, bool WT>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
@@ -407,9 +409,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 #pragma unroll
         for (int u = 0; u < DV; ++u)
             if (i0 + u * kBlock < nvec)
-                store16(d + (i0 + u * kBlock) * 16, v[u]);
+                store_row16<WT>(d + (i0 + u * kBlock) * 16, v[u]);
         if (sc_lane)
-            store16(a.ws + a.off_scales + (int64_t)r * a.region + q * a.srow_bytes + threadIdx.x * 16, sv);
+            store_row16<false>(a.ws + a.off_scales + (int64_t)r * a.region + q * a.srow_bytes + threadIdx.x * 16, sv);
     }
     if (c == 0 && a.srow_bytes && !sc_vec)
         copy_row_any(a.scales + q * a.srow_bytes, a.srow_bytes, mask,
@@ -427,7 +429,7 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 // blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
 // DV: 16-byte vectors per thread in a payload row chunk; PF: row loads
 // before the mask (scatter_chunk).
-template <int KQ, int DV, bool PF>
+template <int KQ, int DV, bool PF, bool WT>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
 {
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     const int64_t first = a.P + plane_blocks;
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
-        scatter_chunk<KQ, DV, PF>(a, w / nchunk, w % nchunk);
+        scatter_chunk<KQ, DV, PF, WT>(a, w / nchunk, w % nchunk);
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
@@ -467,7 +469,7 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
 // ascending rank order, those vectors of row q of every rank in the token's
 // mask.  Expert-output rows are read once (non-temporal loads); the loads
 // of up to G ranks are issued before any is consumed.
-template <int VPT, int G, bool NT_OUT>
+template <int VPT, int G, bool WT>
 __global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
@@ -529,11 +531,7 @@ __global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int
             o[1] = pack_bf16x2(acc[u][2], acc[u][3]);
             o[2] = pack_bf16x2(acc[u][4], acc[u][5]);
             o[3] = pack_bf16x2(acc[u][6], acc[u][7]);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + (i0 + u * kBlock) * 8);
-            if (NT_OUT)
-                __builtin_nontemporal_store(o, dst);
-            else
-                *dst = o;
+            store_row16<WT>(a.out + q * a.H + (i0 + u * kBlock) * 8, o);
         }
     }
 }
@@ -588,7 +586,7 @@ __device__ __forceinline__ void quantise8(u32x4 x, uint32_t &c0, uint32_t &c1, u
 // Each lane owns 8 elements in each half of the chunk (elements
 // c*4096 + h*2048 + lane*8 ..), so every load instruction of a wave covers
 // 1 KB of a row without gaps; four lanes share a block.
-template <int G>
+template <int G, bool WT>
 __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
@@ -639,7 +637,11 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a
                     uint32_t c0, c1, sc;
                     quantise8(x[u][h], c0, c1, sc);
                     if (act[h]) {
-                        *reinterpret_cast<u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]) = u32x2{c0, c1};
+                        if constexpr (WT)
+                            store8_wt(land + a.off_land_codes + slot * a.H + e[h], u32x2{c0, c1});
+                        else
+                            *reinterpret_cast<u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]) =
+                                u32x2{c0, c1};
                         if ((threadIdx.x & 3) == 0)
                             land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)] = (uint8_t)sc;
                     }
@@ -747,8 +749,7 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs 
 #pragma unroll
             for (int j = 0; j < 4; ++j)
                 o[j] = pack_bf16x2(acc[h][2 * j], acc[h][2 * j + 1]);
-            u32x4 *dst = reinterpret_cast<u32x4 *>(a.out + q * a.H + e[h]);
-            __builtin_nontemporal_store(o, dst);
+            store_row16<false>(a.out + q * a.H + e[h], o);
         }
     }
 }
@@ -777,19 +778,26 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     const int64_t grid =
         a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
     const bool pf = S * nchunk <= MOE_EP_PREFETCH_ITEMS;
+    // write-through payload stores: long rows only, and a bound on the
+    // payload bytes written (each token goes to at most min(P, k) ranks)
+    int64_t N = 0;
+    for (int i = 0; i < a.P; ++i)
+        N += a.n[i];
+    const bool wt = long_rows && N * std::min(a.P, a.k) * a.row_bytes <= MOE_EP_WT_BYTES;
     const dim3 g((unsigned)grid), b(kBlock);
-    if (long_rows && pf)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG, true>), g, b, 0, s, a, nplane,
-                           plane_blocks, nchunk);
+    constexpr int L = MOE_EP_DISPATCH_VPT_LONG, Sh = MOE_EP_DISPATCH_VPT_SHORT;
+    if (long_rows && pf && wt)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, L, true, true>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+    else if (long_rows && pf)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, L, true, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+    else if (long_rows && wt)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, L, false, true>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
     else if (long_rows)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_LONG, false>), g, b, 0, s, a, nplane,
-                           plane_blocks, nchunk);
+        hipLaunchKernelGGL((dispatch_kernel<KQ, L, false, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
     else if (pf)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT, true>), g, b, 0, s, a, nplane,
-                           plane_blocks, nchunk);
+        hipLaunchKernelGGL((dispatch_kernel<KQ, Sh, true, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
     else
-        hipLaunchKernelGGL((dispatch_kernel<KQ, MOE_EP_DISPATCH_VPT_SHORT, false>), g, b, 0, s, a, nplane,
-                           plane_blocks, nchunk);
+        hipLaunchKernelGGL((dispatch_kernel<KQ, Sh, false, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
     return hipGetLastError();
 }
 
@@ -807,12 +815,12 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s)
     return launch_dispatch_kq<0>(a, s);
 }
 
-template <int VPT, int G, bool NT_OUT>
+template <int VPT, int G, bool WT>
 static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
 {
     const int64_t nchunk = ceil_div((int64_t)a.H >> 3, kBlock * VPT);
     const int64_t S = (int64_t)a.P * a.T;
-    hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, NT_OUT>), dim3((unsigned)grid_for(S * nchunk)),
+    hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT>), dim3((unsigned)grid_for(S * nchunk)),
                        dim3(kBlock), 0, s, a, nchunk);
     return hipGetLastError();
 }
@@ -820,16 +828,30 @@ static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
 hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s)
 {
     const int64_t out_bytes = (int64_t)a.P * a.T * a.H * 2;
+    const bool wt = out_bytes <= MOE_EP_WT_BYTES;
     if (out_bytes >= MOE_EP_COMBINE_LARGE_BYTES)
-        return launch_combine_shape<MOE_EP_COMBINE_LARGE>(a, s);
-    return launch_combine_shape<MOE_EP_COMBINE_SMALL>(a, s);
+        return wt ? launch_combine_shape<MOE_EP_COMBINE_LARGE, true>(a, s)
+                  : launch_combine_shape<MOE_EP_COMBINE_LARGE, false>(a, s);
+    return wt ? launch_combine_shape<MOE_EP_COMBINE_SMALL, true>(a, s)
+              : launch_combine_shape<MOE_EP_COMBINE_SMALL, false>(a, s);
 }
 
 hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s)
 {
     const int64_t nchunk = ceil_div((int64_t)a.H >> 4, kBlock);
     const dim3 grid((unsigned)grid_for((int64_t)a.P * a.T * nchunk));
-    hipLaunchKernelGGL(combine_fp8_quant_kernel<MOE_EP_FP8_GATHER>, grid, dim3(kBlock), 0, s, a, nchunk);
+    // the quantise pass writes at most P landing rows per token; the landing
+    // codes are written through L2 when that bound is small
+    int64_t N = 0;
+    for (int i = 0; i < a.P; ++i)
+        N += a.n[i];
+    const int64_t land_row = (int64_t)a.H + (a.H >> 5);
+    if (N * a.P * land_row <= MOE_EP_WT_BYTES)
+        hipLaunchKernelGGL((combine_fp8_quant_kernel<MOE_EP_FP8_GATHER, true>), grid, dim3(kBlock), 0, s, a,
+                           nchunk);
+    else
+        hipLaunchKernelGGL((combine_fp8_quant_kernel<MOE_EP_FP8_GATHER, false>), grid, dim3(kBlock), 0, s, a,
+                           nchunk);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
