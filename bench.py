@@ -42,8 +42,8 @@ def traffic_summary_path(config: str) -> str:
     name = "ep8_bf16" if config == "ep8" else config.replace("-", "_")
     return os.path.join(ROOT, "profiles", f"pmc_traffic_{name}.txt")
 # device sources of the kernels the counter summaries describe
-KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f)
-                  for f in ("exchange.hip", "agrs.hip", "formats.h", "memory_ops.h", "moe_ep_internal.h")]
+SOURCE_NAMES = ("exchange.hip", "agrs.hip", "formats.h", "memory_ops.h", "moe_ep_internal.h")
+KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f) for f in SOURCE_NAMES]
 
 
 def source_digest() -> str:
@@ -128,7 +128,7 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
                 f"#   python3 <repo>/bench.py{cfg} --pmc-summary <out>/pmc_fetch/pmc_counter_collection.csv \\\n"
                 "#       <out>/pmc_write/pmc_counter_collection.csv\n"
                 "# source_digest: first 16 hex digits of the sha256 of combine_route_mask_amd/csrc/\n"
-                "# exchange.hip, agrs.hip, formats.h and moe_ep_internal.h, concatenated, with\n"
+                f"# {', '.join(SOURCE_NAMES[:-1])} and {SOURCE_NAMES[-1]}, concatenated, with\n"
                 "# comments and white space removed\n")
         for l in lines:
             f.write(l + "\n")
