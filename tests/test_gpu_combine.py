@@ -265,3 +265,43 @@ def test_combine_fp8_full_ep8_mxfp8():
     eo = _poison(W.draw_expert_output(w.P, w.T, w.H, w.seed, device="cuda"), valid)
     y = ex.combine(eo)
     _check_fp8(c, ex, eo, y, valid)
+
+
+def test_combine_fp8_landing_above_256mib_sampled():
+    """The quantise pass writes its landing codes non-temporally when
+    N * P * (H + H/32) exceeds 256 MiB (here 16 * 8192 * 2112 bytes), and
+    through L2 below (every other FP8 case); sampled tokens against the
+    oracle's per-token FP8 combine."""
+    w = dataclasses.replace(W.EP8_MXFP8, name="fp8 landing 277 MB", fmt="bf16", P=16, E=64, k=8, T=512,
+                            H=2048, n_lo=512, n_hi=512, routing="uniform")
+    log(f"fp8 combine case: {w.name}")
+    c = random_byte_case(w, w.seed)
+    ex = _exchange(w)
+    pl, sc, ids, wt = gpu_inputs(c)
+    ex.dispatch(pl, ids, wt, num_tokens=c.counts.tolist())
+    del pl
+    eo = W.draw_expert_output(w.P, w.T, w.H, w.seed, device="cuda")
+    y = ex.combine(eo)
+    torch.cuda.synchronize()
+    gc, gs = ex.combine_landing()
+    rng = np.random.default_rng(5)
+    for q in rng.choice(w.P * w.T, size=96, replace=False):
+        s, t = divmod(int(q), w.T)
+        rows = bits16(eo[:, q])
+        codes, scales, ref_q, yq = oracle.combine_token_fp8(c.ids[s, t], rows, E=w.E)
+        ref, _ = oracle.combine_token_bf16(c.ids[s, t], rows, E=w.E)
+        owners = {oracle.owner(int(i), w.E, w.P) for i in c.ids[s, t]} - {-1}
+        mag = np.zeros(w.H)
+        floor = np.zeros(w.H)
+        for r in sorted(owners):
+            assert torch.equal(gc[s, r * w.T + t].cpu(), torch.from_numpy(codes[r])), f"codes {s},{t},{r}"
+            assert torch.equal(gs[s, r * w.T + t].cpu(), torch.from_numpy(scales[r])), f"scales {s},{t},{r}"
+            mag += np.abs(bf16_bits_to_f64(rows[r]))
+            floor += np.repeat(2.0 ** (scales[r].astype(np.int64) - 127 - 10), 32)
+        yv = bf16_bits_to_f64(bits16(y[s, t]))
+        acc = max(len(owners) - 1, 0) * 2.0 ** -24 * (1 + 2.0 ** -4) * (mag + floor)
+        assert np.all(np.abs(yv - ref_q) <= 2.0 ** -8 * np.abs(ref_q) + acc + 2.0 ** -126), (s, t)
+        assert np.all(np.abs(yv - ref) <= 0.07 * mag + floor + 2.0 ** -8 * np.abs(ref)), (s, t)
+    ex.destroy()
+    del eo, y, ex, gc, gs
+    torch.cuda.empty_cache()

@@ -179,6 +179,29 @@ def test_dispatch_full_ep64(w):
     torch.cuda.empty_cache()
 
 
+# Long rows (8 KB and more) are stored write-through when the launch's
+# payload writes are bounded by 256 MiB (N * min(P, k) * row) and
+# non-temporally above; the row loads go before the mask in steps of at
+# most 16384 (token, chunk) items.  These two cases take the combinations
+# the other tests miss: a small step above the byte bound, and a large step
+# (many slots) below it.
+STORE_PATHS = [
+    dataclasses.replace(W.TINY, name="long rows, small step, 315 MB of rows", P=8, E=64, k=8, T=300,
+                        H=8192, n_lo=300, n_hi=300),
+    dataclasses.replace(W.TINY, name="long rows, 16640 slots, few tokens", P=64, E=256, k=8, T=260,
+                        H=4096, n_lo=0, n_hi=2),
+]
+
+
+@pytest.mark.parametrize("w", STORE_PATHS, ids=lambda w: w.name)
+def test_dispatch_store_paths(w):
+    c = random_byte_case(w, 41)
+    ex = _run(c, dests=None if w.P <= 8 else [0, 17, 63])
+    ex.destroy()
+    del ex
+    torch.cuda.empty_cache()
+
+
 def test_dispatch_is_deterministic():
     w = dataclasses.replace(W.EP8_BF16, name="determinism", H=1024)
     c = random_byte_case(w, 41)
