@@ -116,6 +116,13 @@ int check_params(const moe_ep_params *pp, Layout *lay)
 
     const int64_t S = (int64_t)p.ep_size * p.max_tokens_per_rank; // slots per region
     const int64_t k = p.top_k;
+    // Every plane is the slot count times a per-slot byte count; capping a
+    // region at 2^46 bytes keeps all of them, the region offsets of 64 ranks
+    // and the kernels' byte products far from int64 overflow.
+    const int64_t per_slot = row + srow + p.extra_payload_bytes_per_token + 8 * k + 4 +
+                             (p.combine_format == MOE_EP_COMBINE_FP8 ? p.hidden_size + p.hidden_size / 32 : 0);
+    if (per_slot > (1ll << 46) / S)
+        return fail(MOE_EP_ERR_CAPACITY, "a workspace region would exceed 2^46 bytes (64 TiB)");
     Layout L;
     std::memset(&L, 0, sizeof L);
     int64_t off = 0;

@@ -140,7 +140,9 @@ int moe_ep_is_supported(void);
 
 /* Bytes of one rank's workspace region for these parameters (every plane
  * 256-byte aligned).  0 when the parameters are invalid (see
- * moe_ep_last_error).  Host-only, no device work. */
+ * moe_ep_last_error), including a region above 2^46 bytes or more than
+ * 2^31 - 1 slots (ep_size * max_tokens_per_rank), which moe_ep_create
+ * rejects with MOE_EP_ERR_CAPACITY.  Host-only, no device work. */
 size_t moe_ep_workspace_bytes(const moe_ep_params *params);
 
 /* Create a handle over a caller-owned device workspace of P regions of
