@@ -365,7 +365,9 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
 // is at most 256 aligned 16-byte words) and the extra payload bytes.  PF: the
 // row loads go out before the id loads of the mask, so the two latencies
 // overlap (a row whose token goes nowhere is then read for nothing); that
-// pays in steps of few workgroups and costs in large ones.
+// pays in steps of few workgroups and costs in large ones.  WT: payload rows
+// are stored write-through, else non-temporally (scale rows always the
+// latter).
 template <int KQ, int DV, bool PF, bool WT>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
@@ -428,7 +430,7 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 // The last two roles loop over their items when there are more items than
 // blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
 // DV: 16-byte vectors per thread in a payload row chunk; PF: row loads
-// before the mask (scatter_chunk).
+// before the mask, WT: write-through payload stores (scatter_chunk).
 template <int KQ, int DV, bool PF, bool WT>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
@@ -585,7 +587,8 @@ __device__ __forceinline__ void quantise8(u32x4 x, uint32_t &c0, uint32_t &c1, u
 // r*T + t; the rows of up to G ranks are loaded before any is quantised.
 // Each lane owns 8 elements in each half of the chunk (elements
 // c*4096 + h*2048 + lane*8 ..), so every load instruction of a wave covers
-// 1 KB of a row without gaps; four lanes share a block.
+// 1 KB of a row without gaps; four lanes share a block.  WT: the codes are
+// stored write-through (launches with few landing bytes), else cached.
 template <int G, bool WT>
 __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
 {

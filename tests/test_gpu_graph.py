@@ -39,6 +39,7 @@ def _capture(fn):
 
 @pytest.mark.parametrize("w", [
     dataclasses.replace(W.EP8_BF16, name="ep8 bf16 graph", H=1024),
+    dataclasses.replace(W.EP8_BF16, name="ep8 bf16 long rows graph (write-through stores)", H=7168),
     dataclasses.replace(W.EP8_MXFP8, name="mxfp8 fp8 graph", T=64, H=512, n_lo=10, n_hi=64),
 ], ids=lambda w: w.name)
 def test_exchange_graph_replays(w):
