@@ -8,7 +8,6 @@ import os
 from fractions import Fraction
 
 import numpy as np
-import pytest
 import torch
 
 import oracle

@@ -5,7 +5,6 @@ mask changes nothing, dead destinations are left untouched, dead sources
 send nothing, combine sums live ranks only."""
 import numpy as np
 import pytest
-import torch
 
 import oracle
 from tests import bruteforce as bf

@@ -23,7 +23,6 @@ on the CPU and upload.
 from __future__ import annotations
 
 import dataclasses
-import math
 from typing import Optional
 
 import numpy as np
