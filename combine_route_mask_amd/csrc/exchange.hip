@@ -359,16 +359,28 @@ __device__ void write_id_planes(const DispatchArgs &a, int r0, int r1, int64_t c
     __syncthreads(); // smask is reused by the block's next item
 }
 
+// True when a side row (scale or extra bytes) of nbytes per token can travel
+// with chunk 0's payload loads: one aligned 16-byte word per lane, at most
+// kBlock words.
+__host__ __device__ __forceinline__ bool side_row_fits(const uint8_t *src, int64_t nbytes, int64_t plane_off,
+                                              int64_t region)
+{
+    return nbytes && (nbytes >> 4) <= kBlock &&
+           (((uint64_t)(uintptr_t)src | (uint64_t)nbytes | (uint64_t)plane_off | (uint64_t)region) & 15) == 0;
+}
+
 // Chunk c of token q's payload row (DV 16-byte vectors per thread, lane
 // strided), read once and stored to every destination in the token's mask;
-// chunk 0 also carries the scale row (loaded with the payload vectors when it
-// is at most 256 aligned 16-byte words) and the extra payload bytes.  PF: the
+// chunk 0 also carries the scale row and the extra payload row (each loaded
+// with the payload vectors when it is at most 256 aligned 16-byte words,
+// else copied after them).  PF: the
 // row loads go out before the id loads of the mask, so the two latencies
 // overlap (a row whose token goes nowhere is then read for nothing); that
 // pays in steps of few workgroups and costs in large ones.  WT: payload rows
 // are stored write-through, else non-temporally (scale rows always the
-// latter).
-template <int KQ, int DV, bool PF, bool WT>
+// latter).  XF: the launch's extra rows fit side_row_fits (a separate
+// instance, as the fused path costs registers where there are none).
+template <int KQ, int DV, bool PF, bool WT, bool XF>
 __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 {
     const int s = (int)(q / a.T);
@@ -390,14 +402,16 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
     for (int u = 0; u < DV; ++u)
         if (i0 + u * kBlock < nvec)
             v[u] = *reinterpret_cast<const u32x4 *>(src + (i0 + u * kBlock) * 16);
-    // a scale row of at most 256 16-byte words travels with chunk 0's loads
-    const bool sc_vec = c == 0 && a.srow_bytes && (a.srow_bytes >> 4) <= kBlock &&
-                        (((uint64_t)(uintptr_t)a.scales | (uint64_t)a.srow_bytes | (uint64_t)a.off_scales |
-                          (uint64_t)a.region) & 15) == 0;
+    const bool sc_vec = c == 0 && side_row_fits(a.scales, a.srow_bytes, a.off_scales, a.region);
+    const bool x_vec = XF && c == 0;
     const bool sc_lane = sc_vec && (int64_t)threadIdx.x < (a.srow_bytes >> 4);
-    u32x4 sv = {0u, 0u, 0u, 0u};
+    const bool x_lane = x_vec && (int64_t)threadIdx.x < (a.xrow_bytes >> 4);
+    u32x4 sv = {0u, 0u, 0u, 0u}, xv = {0u, 0u, 0u, 0u};
     if (sc_lane)
         sv = *reinterpret_cast<const u32x4 *>(a.scales + q * a.srow_bytes + threadIdx.x * 16);
+    if constexpr (XF)
+        if (x_lane)
+            xv = *reinterpret_cast<const u32x4 *>(a.extra + q * a.xrow_bytes + threadIdx.x * 16);
     if (PF) {
         mask = route_mask<KQ>(a, q);
         if (!mask)
@@ -414,11 +428,15 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
                 store_row16<WT>(d + (i0 + u * kBlock) * 16, v[u]);
         if (sc_lane)
             store_row16<false>(a.ws + a.off_scales + (int64_t)r * a.region + q * a.srow_bytes + threadIdx.x * 16, sv);
+        if constexpr (XF)
+            if (x_lane)
+                store_row16<false>(a.ws + a.off_extra + (int64_t)r * a.region + q * a.xrow_bytes + threadIdx.x * 16,
+                                   xv);
     }
     if (c == 0 && a.srow_bytes && !sc_vec)
         copy_row_any(a.scales + q * a.srow_bytes, a.srow_bytes, mask,
                      a.ws + a.off_scales + q * a.srow_bytes, a.region);
-    if (c == 0 && a.xrow_bytes)
+    if (c == 0 && a.xrow_bytes && !x_vec)
         copy_row_any(a.extra + q * a.xrow_bytes, a.xrow_bytes, mask,
                      a.ws + a.off_extra + q * a.xrow_bytes, a.region);
 }
@@ -430,8 +448,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 // The last two roles loop over their items when there are more items than
 // blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
 // DV: 16-byte vectors per thread in a payload row chunk; PF: row loads
-// before the mask, WT: write-through payload stores (scatter_chunk).
-template <int KQ, int DV, bool PF, bool WT>
+// before the mask, WT: write-through payload stores, XF: extra rows loaded
+// with the payload (scatter_chunk).
+template <int KQ, int DV, bool PF, bool WT, bool XF>
 __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_t nplane,
                                                           int64_t plane_blocks, int64_t nchunk)
 {
@@ -452,7 +471,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     const int64_t first = a.P + plane_blocks;
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
-        scatter_chunk<KQ, DV, PF, WT>(a, w / nchunk, w % nchunk);
+        scatter_chunk<KQ, DV, PF, WT, XF>(a, w / nchunk, w % nchunk);
 }
 
 __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
@@ -769,6 +788,18 @@ inline int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
 
 } // namespace
 
+template <int KQ, int DV, bool PF, bool WT>
+static void launch_dispatch_xf(const DispatchArgs &a, bool xf, dim3 g, int64_t nplane, int64_t plane_blocks,
+                               int64_t nchunk, hipStream_t s)
+{
+    if (xf)
+        hipLaunchKernelGGL((dispatch_kernel<KQ, DV, PF, WT, true>), g, dim3(kBlock), 0, s, a, nplane,
+                           plane_blocks, nchunk);
+    else
+        hipLaunchKernelGGL((dispatch_kernel<KQ, DV, PF, WT, false>), g, dim3(kBlock), 0, s, a, nplane,
+                           plane_blocks, nchunk);
+}
+
 template <int KQ>
 static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
 {
@@ -787,20 +818,22 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     for (int i = 0; i < a.P; ++i)
         N += a.n[i];
     const bool wt = long_rows && N * std::min(a.P, a.k) * a.row_bytes <= MOE_EP_WT_BYTES;
-    const dim3 g((unsigned)grid), b(kBlock);
+    // extra rows that fit one word per lane travel with the payload loads
+    const bool xf = side_row_fits(a.extra, a.xrow_bytes, a.off_extra, a.region);
+    const dim3 g((unsigned)grid);
     constexpr int L = MOE_EP_DISPATCH_VPT_LONG, Sh = MOE_EP_DISPATCH_VPT_SHORT;
     if (long_rows && pf && wt)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, L, true, true>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, L, true, true>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (long_rows && pf)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, L, true, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, L, true, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (long_rows && wt)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, L, false, true>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, L, false, true>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (long_rows)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, L, false, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, L, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (pf)
-        hipLaunchKernelGGL((dispatch_kernel<KQ, Sh, true, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, Sh, true, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else
-        hipLaunchKernelGGL((dispatch_kernel<KQ, Sh, false, false>), g, b, 0, s, a, nplane, plane_blocks, nchunk);
+        launch_dispatch_xf<KQ, Sh, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     return hipGetLastError();
 }
 

@@ -36,6 +36,17 @@ CASES = [
     (dataclasses.replace(W.EP8_BF16, name="masked extra + eplb", T=24, H=256, n_lo=0,
                          n_hi=24), 32, 64, [0, 2, 3, 6]),
     (dataclasses.replace(W.EP64_BF16, name="P64 eplb E", T=4, H=64, n_lo=0, n_hi=4), 16, 256, None),
+    # extra rows of at most 256 aligned 16-byte words travel with the payload
+    # loads (long and short rows, small and large steps); longer or unaligned
+    # ones are copied after the payload
+    (dataclasses.replace(W.EP8_BF16, name="router logits 1 KB, long rows", T=64, H=4096, n_lo=0,
+                         n_hi=64), 1024, 0, None),
+    (dataclasses.replace(W.TINY, name="extra 4096B, long rows", P=4, E=16, k=4, T=8, H=8192, n_lo=1,
+                         n_hi=8), 4096, 0, None),
+    (dataclasses.replace(W.TINY, name="extra 4112B copied, long rows", P=4, E=16, k=4, T=8, H=8192,
+                         n_lo=1, n_hi=8), 4112, 0, None),
+    (dataclasses.replace(W.EP64_BF16, name="extra 64B, 16640 slots", T=260, H=64, n_lo=0, n_hi=3),
+     64, 0, None),
 ]
 
 
