@@ -485,76 +485,99 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
     }
 }
 
+// Runs item(w) for the launch's items w < items.  ONE: the grid has one
+// workgroup per item, so a workgroup runs its item and ends; otherwise
+// workgroups loop over the items with the grid's stride.  With no loop, an
+// item's first loads (the combine kernels' route mask) precede every store
+// of the kernel, so the compiler may fetch a uniform one with a scalar load,
+// which it cannot do inside a loop whose earlier passes store (EP8 BF16
+// combine 11.6 -> 10.9 us).
+template <bool ONE, typename F>
+__device__ __forceinline__ void for_each_item(int64_t items, F &&item)
+{
+    if constexpr (ONE) {
+        if ((int64_t)blockIdx.x < items)
+            item((int64_t)blockIdx.x);
+    } else {
+        for (int64_t w = blockIdx.x; w < items; w += gridDim.x)
+            item(w);
+    }
+}
+
 // BF16 combine: item (token q = s*T + t, row chunk c); each thread owns
 // VPT 16-byte vectors (8 bf16 each) of the output row and sums, in fp32 and
 // ascending rank order, those vectors of row q of every rank in the token's
 // mask.  Expert-output rows are read once (non-temporal loads); the loads
 // of up to G ranks are issued before any is consumed.
 template <int VPT, int G, bool WT>
-__global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
+__device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t w, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t rank_bytes = S * a.H * 2;
     const int64_t nvec = a.H >> 3;
-    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
-        const int64_t q = w / nchunk, c = w % nchunk;
-        const int s = (int)(q / a.T);
-        const int t = (int)(q - (int64_t)s * a.T);
-        const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
-        if (t >= a.n[s] || i0 >= nvec)
-            continue;
-        const uint64_t mask = *reinterpret_cast<const uint64_t *>(
-            a.ws + (int64_t)s * a.region + a.off_masks + (int64_t)t * 8);
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2 + i0 * 16;
-        bool in[VPT];
+    const int64_t q = w / nchunk, c = w % nchunk;
+    const int s = (int)(q / a.T);
+    const int t = (int)(q - (int64_t)s * a.T);
+    const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
+    if (t >= a.n[s] || i0 >= nvec)
+        return;
+    const uint64_t mask = *reinterpret_cast<const uint64_t *>(
+        a.ws + (int64_t)s * a.region + a.off_masks + (int64_t)t * 8);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2 + i0 * 16;
+    bool in[VPT];
 #pragma unroll
-        for (int u = 0; u < VPT; ++u)
-            in[u] = i0 + u * kBlock < nvec;
-        float acc[VPT][8];
+    for (int u = 0; u < VPT; ++u)
+        in[u] = i0 + u * kBlock < nvec;
+    float acc[VPT][8];
 #pragma unroll
-        for (int u = 0; u < VPT; ++u)
+    for (int u = 0; u < VPT; ++u)
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                acc[u][e] = 0.0f;
-        uint64_t m = mask;
-        while (m) {
-            int r[G];
-            int cnt = 0;
+        for (int e = 0; e < 8; ++e)
+            acc[u][e] = 0.0f;
+    uint64_t m = mask;
+    while (m) {
+        int r[G];
+        int cnt = 0;
 #pragma unroll
-            for (int g = 0; g < G; ++g) {
-                r[g] = 0;
-                if (m) {
-                    r[g] = __builtin_ctzll(m);
-                    m &= m - 1;
-                    cnt = g + 1;
-                }
+        for (int g = 0; g < G; ++g) {
+            r[g] = 0;
+            if (m) {
+                r[g] = __builtin_ctzll(m);
+                m &= m - 1;
+                cnt = g + 1;
             }
-            u32x4 v[G][VPT];
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int u = 0; u < VPT; ++u)
-                    if (g < cnt && in[u])
-                        v[g][u] = load16_nt(src + (int64_t)r[g] * rank_bytes + u * kBlock * 16);
-#pragma unroll
-            for (int g = 0; g < G; ++g)
-#pragma unroll
-                for (int u = 0; u < VPT; ++u)
-                    if (g < cnt && in[u])
-                        add_bf16x8(acc[u], v[g][u]);
         }
+        u32x4 v[G][VPT];
 #pragma unroll
-        for (int u = 0; u < VPT; ++u) {
-            if (!in[u])
-                continue;
-            u32x4 o;
-            o[0] = pack_bf16x2(acc[u][0], acc[u][1]);
-            o[1] = pack_bf16x2(acc[u][2], acc[u][3]);
-            o[2] = pack_bf16x2(acc[u][4], acc[u][5]);
-            o[3] = pack_bf16x2(acc[u][6], acc[u][7]);
-            store_row16<WT>(a.out + q * a.H + (i0 + u * kBlock) * 8, o);
-        }
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int u = 0; u < VPT; ++u)
+                if (g < cnt && in[u])
+                    v[g][u] = load16_nt(src + (int64_t)r[g] * rank_bytes + u * kBlock * 16);
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+            for (int u = 0; u < VPT; ++u)
+                if (g < cnt && in[u])
+                    add_bf16x8(acc[u], v[g][u]);
     }
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+        if (!in[u])
+            continue;
+        u32x4 o;
+        o[0] = pack_bf16x2(acc[u][0], acc[u][1]);
+        o[1] = pack_bf16x2(acc[u][2], acc[u][3]);
+        o[2] = pack_bf16x2(acc[u][4], acc[u][5]);
+        o[3] = pack_bf16x2(acc[u][6], acc[u][7]);
+        store_row16<WT>(a.out + q * a.H + (i0 + u * kBlock) * 8, o);
+    }
+}
+
+template <int VPT, int G, bool WT, bool ONE>
+__global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
+{
+    for_each_item<ONE>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { combine_bf16_item<VPT, G, WT>(a, w, nchunk); });
 }
 
 // e4m3 codes (two words, element 0 in the lowest byte) and e8m0 scale code
@@ -609,68 +632,74 @@ __device__ __forceinline__ void quantise8(u32x4 x, uint32_t &c0, uint32_t &c1, u
 // 1 KB of a row without gaps; four lanes share a block.  WT: the codes are
 // stored write-through (launches with few landing bytes), else cached.
 template <int G, bool WT>
-__global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
+__device__ __forceinline__ void fp8_quant_item(const CombineArgs &a, int64_t w, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t rank_bytes = S * a.H * 2;
-    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
-        const int64_t q = w / nchunk, c = w % nchunk;
-        const int s = (int)(q / a.T);
-        const int t = (int)(q - (int64_t)s * a.T);
-        if (t >= a.n[s])
-            continue;
-        int64_t e[2];
-        bool act[2]; // H % 32 == 0: the four lanes of a block agree
+    const int64_t q = w / nchunk, c = w % nchunk;
+    const int s = (int)(q / a.T);
+    const int t = (int)(q - (int64_t)s * a.T);
+    if (t >= a.n[s])
+        return;
+    int64_t e[2];
+    bool act[2]; // H % 32 == 0: the four lanes of a block agree
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
-            act[h] = e[h] < a.H;
-        }
-        uint8_t *land = a.ws + (int64_t)s * a.region;
-        const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
-        const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2;
-        uint64_t m = mask;
-        while (m) {
-            int r[G];
-            int cnt = 0;
+    for (int h = 0; h < 2; ++h) {
+        e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
+        act[h] = e[h] < a.H;
+    }
+    uint8_t *land = a.ws + (int64_t)s * a.region;
+    const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
+    const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2;
+    uint64_t m = mask;
+    while (m) {
+        int r[G];
+        int cnt = 0;
 #pragma unroll
-            for (int u = 0; u < G; ++u) {
-                r[u] = 0;
-                if (m) {
-                    r[u] = __builtin_ctzll(m);
-                    m &= m - 1;
-                    cnt = u + 1;
-                }
+        for (int u = 0; u < G; ++u) {
+            r[u] = 0;
+            if (m) {
+                r[u] = __builtin_ctzll(m);
+                m &= m - 1;
+                cnt = u + 1;
             }
-            u32x4 x[G][2];
+        }
+        u32x4 x[G][2];
 #pragma unroll
-            for (int u = 0; u < G; ++u)
+        for (int u = 0; u < G; ++u)
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    x[u][h] = (act[h] && u < cnt) ? load16_nt(src + (int64_t)r[u] * rank_bytes + e[h] * 2)
-                                                  : u32x4{0u, 0u, 0u, 0u};
+            for (int h = 0; h < 2; ++h)
+                x[u][h] = (act[h] && u < cnt) ? load16_nt(src + (int64_t)r[u] * rank_bytes + e[h] * 2)
+                                              : u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
-            for (int u = 0; u < G; ++u) {
-                if (u >= cnt)
-                    break;
-                const int64_t slot = (int64_t)r[u] * a.T + t;
+        for (int u = 0; u < G; ++u) {
+            if (u >= cnt)
+                break;
+            const int64_t slot = (int64_t)r[u] * a.T + t;
 #pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    uint32_t c0, c1, sc;
-                    quantise8(x[u][h], c0, c1, sc);
-                    if (act[h]) {
-                        if constexpr (WT)
-                            store8_wt(land + a.off_land_codes + slot * a.H + e[h], u32x2{c0, c1});
-                        else
-                            *reinterpret_cast<u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]) =
-                                u32x2{c0, c1};
-                        if ((threadIdx.x & 3) == 0)
-                            land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)] = (uint8_t)sc;
-                    }
+            for (int h = 0; h < 2; ++h) {
+                uint32_t c0, c1, sc;
+                quantise8(x[u][h], c0, c1, sc);
+                if (act[h]) {
+                    if constexpr (WT)
+                        store8_wt(land + a.off_land_codes + slot * a.H + e[h], u32x2{c0, c1});
+                    else
+                        *reinterpret_cast<u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]) =
+                            u32x2{c0, c1};
+                    if ((threadIdx.x & 3) == 0)
+                        land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)] = (uint8_t)sc;
                 }
             }
         }
     }
+}
+
+// Looping over items (no one-item launches): on the MXFP8 workload the
+// one-item form made both FP8 kernels 1-3% slower.
+template <int G, bool WT>
+__global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
+{
+    for_each_item<false>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { fp8_quant_item<G, WT>(a, w, nchunk); });
 }
 
 // FP8 combine, receiving side: item (token q = s*T + t, chunk c of 4096
@@ -680,100 +709,103 @@ __global__ __launch_bounds__(kBlock) void combine_fp8_quant_kernel(CombineArgs a
 // them in fp32 in ascending rank order, rounds to bf16 and stores the output
 // non-temporally (it is not read again in the step).
 template <int G>
-__global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs a, int64_t nchunk)
+__device__ __forceinline__ void fp8_gather_item(const CombineArgs &a, int64_t w, int64_t nchunk)
 {
-    const int64_t S = (int64_t)a.P * a.T;
-    for (int64_t w = blockIdx.x; w < S * nchunk; w += gridDim.x) {
-        const int64_t q = w / nchunk, c = w % nchunk;
-        const int s = (int)(q / a.T);
-        const int t = (int)(q - (int64_t)s * a.T);
-        int64_t e[2];
-        bool act[2];
+    const int64_t q = w / nchunk, c = w % nchunk;
+    const int s = (int)(q / a.T);
+    const int t = (int)(q - (int64_t)s * a.T);
+    int64_t e[2];
+    bool act[2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
-            act[h] = e[h] < a.H;
+    for (int h = 0; h < 2; ++h) {
+        e[h] = c * (kBlock * 16) + h * (kBlock * 8) + threadIdx.x * 8;
+        act[h] = e[h] < a.H;
+    }
+    if (t >= a.n[s] || !act[0])
+        return;
+    const uint8_t *land = a.ws + (int64_t)s * a.region;
+    const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
+    float acc[2][8];
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+            acc[h][j] = 0.0f;
+    uint64_t m = mask;
+    while (m) {
+        int r[G];
+        int cnt = 0;
+#pragma unroll
+        for (int u = 0; u < G; ++u) {
+            r[u] = 0;
+            if (m) {
+                r[u] = __builtin_ctzll(m);
+                m &= m - 1;
+                cnt = u + 1;
+            }
         }
-        if (t >= a.n[s] || !act[0])
-            continue;
-        const uint8_t *land = a.ws + (int64_t)s * a.region;
-        const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
-        float acc[2][8];
+        u32x2 cv[G][2];
+        uint32_t sc[G][2];
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                acc[h][j] = 0.0f;
-        uint64_t m = mask;
-        while (m) {
-            int r[G];
-            int cnt = 0;
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                r[u] = 0;
-                if (m) {
-                    r[u] = __builtin_ctzll(m);
-                    m &= m - 1;
-                    cnt = u + 1;
-                }
-            }
-            u32x2 cv[G][2];
-            uint32_t sc[G][2];
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                if (u < cnt) {
-                    const int64_t slot = (int64_t)r[u] * a.T + t;
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        if (act[h]) {
-                            cv[u][h] = __builtin_nontemporal_load(
-                                reinterpret_cast<const u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]));
-                            sc[u][h] = land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)];
-                        }
-                    }
-                }
-            }
-#pragma unroll
-            for (int u = 0; u < G; ++u) {
-                if (u >= cnt)
-                    break;
+        for (int u = 0; u < G; ++u) {
+            if (u < cnt) {
+                const int64_t slot = (int64_t)r[u] * a.T + t;
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
-                    if (!act[h])
-                        continue;
-                    if (sc[u][h] == 0xFFu) {
-#pragma unroll
-                        for (int j = 0; j < 8; ++j)
-                            acc[h][j] = __uint_as_float(0x7FC00000u);
-                        continue;
-                    }
-                    // v_cvt_scalef32_pk_f32_fp8 decodes two codes (low byte
-                    // first) and multiplies them by the scale 2^(sc - 127),
-                    // exactly, subnormal scales included
-                    const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sc[u][h] - 127);
-#pragma unroll
-                    for (int j = 0; j < 2; ++j) {
-                        const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, false);
-                        const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, true);
-                        acc[h][4 * j] += lo[0];
-                        acc[h][4 * j + 1] += lo[1];
-                        acc[h][4 * j + 2] += hi[0];
-                        acc[h][4 * j + 3] += hi[1];
+                    if (act[h]) {
+                        cv[u][h] = __builtin_nontemporal_load(
+                            reinterpret_cast<const u32x2 *>(land + a.off_land_codes + slot * a.H + e[h]));
+                        sc[u][h] = land[a.off_land_scales + slot * (a.H >> 5) + (e[h] >> 5)];
                     }
                 }
             }
         }
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            if (!act[h])
-                continue;
-            u32x4 o;
+        for (int u = 0; u < G; ++u) {
+            if (u >= cnt)
+                break;
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                o[j] = pack_bf16x2(acc[h][2 * j], acc[h][2 * j + 1]);
-            store_row16<false>(a.out + q * a.H + e[h], o);
+            for (int h = 0; h < 2; ++h) {
+                if (!act[h])
+                    continue;
+                if (sc[u][h] == 0xFFu) {
+#pragma unroll
+                    for (int j = 0; j < 8; ++j)
+                        acc[h][j] = __uint_as_float(0x7FC00000u);
+                    continue;
+                }
+                // v_cvt_scalef32_pk_f32_fp8 decodes two codes (low byte
+                // first) and multiplies them by the scale 2^(sc - 127),
+                // exactly, subnormal scales included
+                const float scale = __builtin_amdgcn_ldexpf(1.0f, (int)sc[u][h] - 127);
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const f32x2 lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, false);
+                    const f32x2 hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8((int)cv[u][h][j], scale, true);
+                    acc[h][4 * j] += lo[0];
+                    acc[h][4 * j + 1] += lo[1];
+                    acc[h][4 * j + 2] += hi[0];
+                    acc[h][4 * j + 3] += hi[1];
+                }
+            }
         }
     }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (!act[h])
+            continue;
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            o[j] = pack_bf16x2(acc[h][2 * j], acc[h][2 * j + 1]);
+        store_row16<false>(a.out + q * a.H + e[h], o);
+    }
+}
+
+template <int G>
+__global__ __launch_bounds__(kBlock) void combine_fp8_gather_kernel(CombineArgs a, int64_t nchunk)
+{
+    for_each_item<false>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { fp8_gather_item<G>(a, w, nchunk); });
 }
 
 // Grid of nitems workgroups capped at 64 rounds of the chip (256 CUs x 8
@@ -855,9 +887,12 @@ template <int VPT, int G, bool WT>
 static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
 {
     const int64_t nchunk = ceil_div((int64_t)a.H >> 3, kBlock * VPT);
-    const int64_t S = (int64_t)a.P * a.T;
-    hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT>), dim3((unsigned)grid_for(S * nchunk)),
-                       dim3(kBlock), 0, s, a, nchunk);
+    const int64_t items = (int64_t)a.P * a.T * nchunk;
+    const dim3 grid((unsigned)grid_for(items));
+    if ((int64_t)grid.x == items)
+        hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT, true>), grid, dim3(kBlock), 0, s, a, nchunk);
+    else
+        hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT, false>), grid, dim3(kBlock), 0, s, a, nchunk);
     return hipGetLastError();
 }
 
