@@ -82,6 +82,25 @@ constexpr int kWaves = kBlock / 64;
 constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
 constexpr int kPlaneGroup = 8;          // destinations per id-plane item
 
+// Runs item(w) for the launch's items w < items.  ONE: the grid has one
+// workgroup per item, so a workgroup runs its item and ends; otherwise
+// workgroups loop over the items with the grid's stride.  With no loop, an
+// item's first loads (a token's ids or route mask) precede every store
+// of the kernel, so the compiler may fetch a uniform one with a scalar load,
+// which it cannot do inside a loop whose earlier passes store (EP8 BF16
+// combine 11.4 -> 10.9 us).
+template <bool ONE, typename F>
+__device__ __forceinline__ void for_each_item(int64_t items, F &&item)
+{
+    if constexpr (ONE) {
+        if ((int64_t)blockIdx.x < items)
+            item((int64_t)blockIdx.x);
+    } else {
+        for (int64_t w = blockIdx.x; w < items; w += gridDim.x)
+            item(w);
+    }
+}
+
 // A 16-byte row store: write-through (WT) or non-temporal.
 template <bool WT>
 __device__ __forceinline__ void store_row16(void *p, u32x4 v)
@@ -469,6 +488,18 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     }
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t first = a.P + plane_blocks;
+    // A prefetching launch has a workgroup for every payload item.  With long
+    // rows each one runs its item without a loop, so the token's ids come in
+    // one scalar load (EP8 dispatch -1%); short rows keep the loop (the
+    // one-item form cost the MXFP8 dispatch 2-3%).
+    static_assert(MOE_EP_PREFETCH_ITEMS <= MOE_EP_SCATTER_GRID, "prefetching launches need one workgroup per item");
+    constexpr bool one = PF && DV == MOE_EP_DISPATCH_VPT_LONG;
+    if constexpr (one) {
+        const int64_t w = b - first;
+        if (w < S * nchunk)
+            scatter_chunk<KQ, DV, PF, WT, XF>(a, w / nchunk, w % nchunk);
+        return;
+    }
     const int64_t stride = (int64_t)gridDim.x - first;
     for (int64_t w = b - first; w < S * nchunk; w += stride)
         scatter_chunk<KQ, DV, PF, WT, XF>(a, w / nchunk, w % nchunk);
@@ -482,25 +513,6 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
         unpack_bf16x2(v[e], lo, hi);
         acc[2 * e] += lo;
         acc[2 * e + 1] += hi;
-    }
-}
-
-// Runs item(w) for the launch's items w < items.  ONE: the grid has one
-// workgroup per item, so a workgroup runs its item and ends; otherwise
-// workgroups loop over the items with the grid's stride.  With no loop, an
-// item's first loads (the combine kernels' route mask) precede every store
-// of the kernel, so the compiler may fetch a uniform one with a scalar load,
-// which it cannot do inside a loop whose earlier passes store (EP8 BF16
-// combine 11.6 -> 10.9 us).
-template <bool ONE, typename F>
-__device__ __forceinline__ void for_each_item(int64_t items, F &&item)
-{
-    if constexpr (ONE) {
-        if ((int64_t)blockIdx.x < items)
-            item((int64_t)blockIdx.x);
-    } else {
-        for (int64_t w = blockIdx.x; w < items; w += gridDim.x)
-            item(w);
     }
 }
 
