@@ -29,6 +29,12 @@ CASES = [
     (dataclasses.replace(W.AGRS16, name="P1", P=1, H=64), [9]),
     (dataclasses.replace(W.AGRS16, name="odd rows", P=5, H=8200, k=3), [2, 1, 4, 3, 1]),
     (dataclasses.replace(W.AGRS16, name="P64", P=64, H=128, k=2), None),
+    # empty first / last segments with a partial last row chunk (the rank of
+    # a row is found before lanes past the row's end leave the item)
+    (dataclasses.replace(W.AGRS16, name="lead and trail zeros, ragged rows", P=5, H=8200, k=3),
+     [0, 3, 0, 2, 0]),
+    (dataclasses.replace(W.AGRS16, name="P64 sparse, ragged rows", P=64, H=136, k=2),
+     [0, 2] + [0] * 29 + [1] + [0] * 30 + [0, 3]),
 ]
 
 
