@@ -423,17 +423,24 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
     """Markdown table of per-launch exchange-kernel durations from a
     rocprofv3 kernel-trace CSV of a bench run, grouped by workload (a new
     workload starts at the first random-input kernel after exchange
-    kernels have run), kernel instance and grid.  A launch that follows a
-    1 GiB cache flush counts as cold; the first launch of an instance in a
-    workload is left out (warm-up)."""
+    kernels have run), kernel instance, grid, cache state and context.  A
+    launch that follows a 1 GiB cache flush counts as cold.  Context "step":
+    a kernel of the other side of the exchange (dispatch side: dispatch,
+    all-gatherv; combine side: the combine kernels, reduce-scatterv) ran
+    since this instance's previous launch, as in the step graphs; "alone":
+    none did, as in the per-kernel graphs whose launch times the bench
+    reports.  The first launch of an instance in a workload is left out
+    (warm-up)."""
     import collections
     import csv
     import re
     import statistics
     ours = ("dispatch_kernel", "combine_bf16_kernel", "combine_fp8_quant_kernel",
             "combine_fp8_gather_kernel", "allgatherv_kernel", "reduce_scatterv_kernel")
+    dispatch_side = ("dispatch_kernel", "allgatherv_kernel")
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
     phase, ran, after_flush, seen = 0, False, False, set()
+    sides_since = collections.defaultdict(set)  # instance -> sides launched since its last launch
     groups = collections.defaultdict(list)
     for r in rows:
         name = r["Kernel_Name"]
@@ -448,17 +455,23 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
             continue
         ran = True
         inst, cold, after_flush = m.group(1), after_flush, False
+        side = "dispatch" if inst.startswith(dispatch_side) else "combine"
+        ctx = "step" if (sides_since[inst] - {side}) else "alone"
+        sides_since[inst] = set()
+        for other in sides_since:
+            if other != inst:
+                sides_since[other].add(side)
         if (phase, inst) not in seen:
             seen.add((phase, inst))
             continue
         wg = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-        groups[(phase, inst, wg, "cold" if cold else "warm")].append(dur)
-    out = ["| workload | kernel | workgroups | cache | launches | mean us | median us | min us |",
-           "|---|---|---|---|---|---|---|---|"]
-    for (ph, inst, wg, c), d in sorted(groups.items()):
+        groups[(phase, inst, wg, "cold" if cold else "warm", ctx)].append(dur)
+    out = ["| workload | kernel | workgroups | cache | context | launches | mean us | median us | min us |",
+           "|---|---|---|---|---|---|---|---|---|"]
+    for (ph, inst, wg, c, ctx), d in sorted(groups.items()):
         label = workloads[ph] if ph < len(workloads) else str(ph)
-        out.append(f"| {label} | `{inst}` | {wg} | {c} | {len(d)} | {statistics.mean(d):.1f} | "
+        out.append(f"| {label} | `{inst}` | {wg} | {c} | {ctx} | {len(d)} | {statistics.mean(d):.1f} | "
                    f"{statistics.median(d):.1f} | {min(d):.1f} |")
     return "\n".join(out) + "\n"
 

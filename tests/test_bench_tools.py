@@ -1,6 +1,7 @@
 """The bench's profile post-processing on small synthetic rocprofv3 CSVs:
-the kernel-trace table (workload phases, cold launches, warm-up launch left
-out) and the counter summary (scaled by the calibration copy)."""
+the kernel-trace table (workload phases, cold launches, launch context,
+warm-up launch left out) and the counter summary (scaled by the calibration
+copy)."""
 import csv
 import json
 
@@ -47,10 +48,26 @@ def test_trace_summary_phases_and_cold(tmp_path):
     lines = bench.trace_summary(str(p), ["first", "second"]).splitlines()
     rows = [l.split("|")[1:-1] for l in lines[2:]]
     rows = [[c.strip() for c in r] for r in rows]
-    assert ["first", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "2", "13.0", "13.0", "12.0"] in rows
-    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "cold", "1", "20.0", "20.0", "20.0"] in rows
-    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "1", "12.0", "12.0", "12.0"] in rows
-    assert not any(r[1].startswith("`combine") and r[0] == "first" and r[4] != "1" for r in rows)
+    assert ["first", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "alone", "2", "13.0", "13.0", "12.0"] in rows
+    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "cold", "alone", "1", "20.0", "20.0", "20.0"] in rows
+    assert ["second", "`dispatch_kernel<2, 4, true>`", "1036", "warm", "alone", "1", "12.0", "12.0", "12.0"] in rows
+    assert not any(r[1].startswith("`combine") and r[0] == "first" for r in rows)
+
+
+def test_trace_summary_context(tmp_path):
+    """Launches alternating with the other side of the exchange are "step",
+    back-to-back launches of one kernel "alone"."""
+    p = tmp_path / "trace.csv"
+    D, C = (DISPATCH, 1036 * 256), (COMBINE, 4096 * 256)
+    _trace(p, [(NORMAL, 2048 * 256, 500), (*D, 90000), (*C, 90000),   # warm-up launches
+               (*D, 10000), (*C, 20000), (*D, 11000), (*C, 21000),     # step graph
+               (*D, 30000), (*D, 31000), (*C, 40000), (*C, 41000)])    # per-kernel graphs
+    lines = bench.trace_summary(str(p), ["wl"]).splitlines()
+    rows = [[c.strip() for c in l.split("|")[1:-1]] for l in lines[2:]]
+    got = {(r[1].split("<")[0].strip("`"), r[4]): (r[5], r[6]) for r in rows}
+    assert got == {("dispatch_kernel", "step"): ("3", "17.0"), ("dispatch_kernel", "alone"): ("1", "31.0"),
+                   ("combine_bf16_kernel", "step"): ("3", "27.0"),
+                   ("combine_bf16_kernel", "alone"): ("1", "41.0")}
 
 
 def _pmc(path, entries):
