@@ -213,8 +213,9 @@ def _need(cond: bool, msg: str):
         raise MoeEpArgError(ERR_INVALID_ARG, msg)
 
 
-def _dev_contig(t, name):
+def _dev_contig(t, name, device=None):
     _need(t.is_cuda, f"{name} must be a GPU tensor")
+    _need(device is None or t.device == device, f"{name} must be on {device}, got {t.device}")
     _need(t.is_contiguous(), f"{name} must be contiguous")
 
 
@@ -280,8 +281,8 @@ class MoeEpExchange:
         P = self.P
         T = runtime_max_tokens_per_rank or self.params.max_tokens_per_rank
         _need(1 <= T <= self.params.max_tokens_per_rank, "T must be in [1, max_tokens_per_rank]")
-        _dev_contig(hidden, "hidden")
-        _dev_contig(topk_ids, "topk_ids")
+        _dev_contig(hidden, "hidden", self.workspace.device)
+        _dev_contig(topk_ids, "topk_ids", self.workspace.device)
         _need(hidden.dim() >= 2 and hidden.shape[0] == P and hidden.shape[1] == T,
               f"hidden must be [P={P}, T={T}, row], got {tuple(hidden.shape)}")
         row, srow = self.row_bytes()
@@ -290,24 +291,24 @@ class MoeEpExchange:
         _need(topk_ids.dtype == torch.int32 and tuple(topk_ids.shape) == (P, T, self.params.top_k),
               "topk_ids must be int32 [P, T, top_k]")
         if topk_weights is not None:
-            _dev_contig(topk_weights, "topk_weights")
+            _dev_contig(topk_weights, "topk_weights", self.workspace.device)
             _need(topk_weights.dtype == torch.float32 and topk_weights.shape == topk_ids.shape,
                   "topk_weights must be float32 [P, T, top_k]")
         if scales is not None:
-            _dev_contig(scales, "scales")
+            _dev_contig(scales, "scales", self.workspace.device)
             _need(scales.dim() >= 2 and scales.shape[0] == P and scales.shape[1] == T and
                   scales.numel() * scales.element_size() == P * T * srow,
                   f"scales must be [P, T] rows of {srow} bytes")
         if extra_payload is not None:
             xb = self.params.extra_payload_bytes_per_token
-            _dev_contig(extra_payload, "extra_payload")
+            _dev_contig(extra_payload, "extra_payload", self.workspace.device)
             _need(extra_payload.dim() >= 2 and extra_payload.shape[0] == P and
                   extra_payload.shape[1] == T and
                   extra_payload.numel() * extra_payload.element_size() == P * T * xb,
                   f"extra_payload must be [P, T] rows of {xb} bytes")
         if eplb_local_stats is not None:
             n = self.params.eplb_stats_num_experts
-            _dev_contig(eplb_local_stats, "eplb_local_stats")
+            _dev_contig(eplb_local_stats, "eplb_local_stats", self.workspace.device)
             _need(eplb_local_stats.dtype == torch.int32 and
                   tuple(eplb_local_stats.shape) == (P, n),
                   f"eplb_local_stats must be int32 [P, {n}]")
@@ -356,12 +357,12 @@ class MoeEpExchange:
         P, H = self.P, self.params.hidden_size
         _need(self.views is not None, "combine before any dispatch")
         T = self.views.tokens_per_rank
-        _dev_contig(expert_output, "expert_output")
+        _dev_contig(expert_output, "expert_output", self.workspace.device)
         _need(expert_output.dtype == torch.bfloat16 and tuple(expert_output.shape) == (P, P * T, H),
               f"expert_output must be bf16 [P, P*T, H] = [{P}, {P * T}, {H}]")
         if output is None:
             output = torch.zeros((P, T, H), dtype=torch.bfloat16, device=expert_output.device)
-        _dev_contig(output, "output")
+        _dev_contig(output, "output", self.workspace.device)
         _need(output.dtype == torch.bfloat16 and tuple(output.shape) == (P, T, H),
               "output must be bf16 [P, T, H]")
         moe_ep_combine(self.handle, expert_output, output, stream)
@@ -373,9 +374,11 @@ def allgatherv(sizes: Sequence[int], tensors, outs, stream=None):
     stacked outputs ``[P, sum(sizes), ...]`` (one launch for all planes)."""
     planes = []
     P, total = len(sizes), int(sum(sizes))
+    _need(P >= 1 and len(tensors) == len(outs) >= 1, "need sizes for P >= 1 ranks and one output per input")
+    dev = tensors[0].device
     for x, o in zip(tensors, outs):
-        _dev_contig(x, "input")
-        _dev_contig(o, "output")
+        _dev_contig(x, "input", dev)
+        _dev_contig(o, "output", dev)
         _need(x.shape[0] == P and o.shape[0] == P, "inputs and outputs are stacked [P, rows, ...]")
         _need(max(sizes) <= x.shape[1], "an input holds fewer rows than its size")
         _need(o.shape[1] >= total and o.shape[2:] == x.shape[2:] and o.dtype == x.dtype,
@@ -391,9 +394,10 @@ def reduce_scatterv(sizes: Sequence[int], partial, out, stream=None):
     """Reduce-scatterv of stacked bf16 partials ``[P, sum(sizes), H]`` into
     ``out`` ``[P, max(sizes), H]`` (rank r's first sizes[r] rows)."""
     _dev_contig(partial, "partial")
-    _dev_contig(out, "out")
+    _dev_contig(out, "out", partial.device)
     import torch
     P, total = len(sizes), int(sum(sizes))
+    _need(P >= 1, "need sizes for P >= 1 ranks")
     _need(partial.dtype == torch.bfloat16 and out.dtype == torch.bfloat16, "bf16 tensors only")
     _need(partial.dim() == 3 and partial.shape[0] == P and partial.shape[1] >= total,
           "partial must be [P, >= sum(sizes), H]")
