@@ -61,6 +61,13 @@
 #ifndef MOE_EP_COMBINE_LARGE
 #define MOE_EP_COMBINE_LARGE 4, 2
 #endif
+// Threads per workgroup of the small-output shape: at H = 7168 a row is
+// 896 16-byte vectors, seven chunks of 128 with no idle lanes (256-thread
+// workgroups leave half of every fourth one idle).  Measured on the EP8
+// step against 256 / 448 / 64 threads: 22.5 against 23.0 / 23.0 / 22.6 us.
+#ifndef MOE_EP_COMBINE_SMALL_BLOCK
+#define MOE_EP_COMBINE_SMALL_BLOCK 128
+#endif
 #ifndef MOE_EP_FP8_GATHER
 #define MOE_EP_FP8_GATHER 2 // ranks per round in the FP8 combine kernels
 #endif
@@ -516,12 +523,13 @@ __device__ __forceinline__ void add_bf16x8(float (&acc)[8], u32x4 v)
     }
 }
 
-// BF16 combine: item (token q = s*T + t, row chunk c); each thread owns
+// BF16 combine: item (token q = s*T + t, row chunk c of BS*VPT vectors,
+// BS threads per workgroup); each thread owns
 // VPT 16-byte vectors (8 bf16 each) of the output row and sums, in fp32 and
 // ascending rank order, those vectors of row q of every rank in the token's
 // mask.  Expert-output rows are read once (non-temporal loads); the loads
 // of up to G ranks are issued before any is consumed.
-template <int VPT, int G, bool WT>
+template <int BS, int VPT, int G, bool WT>
 __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t w, int64_t nchunk)
 {
     const int64_t S = (int64_t)a.P * a.T;
@@ -530,7 +538,7 @@ __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t 
     const int64_t q = w / nchunk, c = w % nchunk;
     const int s = (int)(q / a.T);
     const int t = (int)(q - (int64_t)s * a.T);
-    const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
+    const int64_t i0 = c * (BS * VPT) + threadIdx.x;
     if (t >= a.n[s] || i0 >= nvec)
         return;
     const uint64_t mask = *reinterpret_cast<const uint64_t *>(
@@ -539,7 +547,7 @@ __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t 
     bool in[VPT];
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
-        in[u] = i0 + u * kBlock < nvec;
+        in[u] = i0 + u * BS < nvec;
     float acc[VPT][8];
 #pragma unroll
     for (int u = 0; u < VPT; ++u)
@@ -565,7 +573,7 @@ __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t 
 #pragma unroll
             for (int u = 0; u < VPT; ++u)
                 if (g < cnt && in[u])
-                    v[g][u] = load16_nt(src + (int64_t)r[g] * rank_bytes + u * kBlock * 16);
+                    v[g][u] = load16_nt(src + (int64_t)r[g] * rank_bytes + u * BS * 16);
 #pragma unroll
         for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -582,14 +590,14 @@ __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t 
         o[1] = pack_bf16x2(acc[u][2], acc[u][3]);
         o[2] = pack_bf16x2(acc[u][4], acc[u][5]);
         o[3] = pack_bf16x2(acc[u][6], acc[u][7]);
-        store_row16<WT>(a.out + q * a.H + (i0 + u * kBlock) * 8, o);
+        store_row16<WT>(a.out + q * a.H + (i0 + u * BS) * 8, o);
     }
 }
 
-template <int VPT, int G, bool WT, bool ONE>
-__global__ __launch_bounds__(kBlock) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
+template <int BS, int VPT, int G, bool WT, bool ONE>
+__global__ __launch_bounds__(BS) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
 {
-    for_each_item<ONE>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { combine_bf16_item<VPT, G, WT>(a, w, nchunk); });
+    for_each_item<ONE>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { combine_bf16_item<BS, VPT, G, WT>(a, w, nchunk); });
 }
 
 // e4m3 codes (two words, element 0 in the lowest byte) and e8m0 scale code
@@ -895,16 +903,16 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s)
     return launch_dispatch_kq<0>(a, s);
 }
 
-template <int VPT, int G, bool WT>
+template <int BS, int VPT, int G, bool WT>
 static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
 {
-    const int64_t nchunk = ceil_div((int64_t)a.H >> 3, kBlock * VPT);
+    const int64_t nchunk = ceil_div((int64_t)a.H >> 3, BS * VPT);
     const int64_t items = (int64_t)a.P * a.T * nchunk;
     const dim3 grid((unsigned)grid_for(items));
     if ((int64_t)grid.x == items)
-        hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT, true>), grid, dim3(kBlock), 0, s, a, nchunk);
+        hipLaunchKernelGGL((combine_bf16_kernel<BS, VPT, G, WT, true>), grid, dim3(BS), 0, s, a, nchunk);
     else
-        hipLaunchKernelGGL((combine_bf16_kernel<VPT, G, WT, false>), grid, dim3(kBlock), 0, s, a, nchunk);
+        hipLaunchKernelGGL((combine_bf16_kernel<BS, VPT, G, WT, false>), grid, dim3(BS), 0, s, a, nchunk);
     return hipGetLastError();
 }
 
@@ -913,10 +921,10 @@ hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s)
     const int64_t out_bytes = (int64_t)a.P * a.T * a.H * 2;
     const bool wt = out_bytes <= MOE_EP_WT_BYTES;
     if (out_bytes >= MOE_EP_COMBINE_LARGE_BYTES)
-        return wt ? launch_combine_shape<MOE_EP_COMBINE_LARGE, true>(a, s)
-                  : launch_combine_shape<MOE_EP_COMBINE_LARGE, false>(a, s);
-    return wt ? launch_combine_shape<MOE_EP_COMBINE_SMALL, true>(a, s)
-              : launch_combine_shape<MOE_EP_COMBINE_SMALL, false>(a, s);
+        return wt ? launch_combine_shape<kBlock, MOE_EP_COMBINE_LARGE, true>(a, s)
+                  : launch_combine_shape<kBlock, MOE_EP_COMBINE_LARGE, false>(a, s);
+    return wt ? launch_combine_shape<MOE_EP_COMBINE_SMALL_BLOCK, MOE_EP_COMBINE_SMALL, true>(a, s)
+              : launch_combine_shape<MOE_EP_COMBINE_SMALL_BLOCK, MOE_EP_COMBINE_SMALL, false>(a, s);
 }
 
 hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s)
