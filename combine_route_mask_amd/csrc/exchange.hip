@@ -68,6 +68,9 @@
 #ifndef MOE_EP_COMBINE_SMALL_BLOCK
 #define MOE_EP_COMBINE_SMALL_BLOCK 128
 #endif
+#ifndef MOE_EP_COMBINE_LARGE_BLOCK
+#define MOE_EP_COMBINE_LARGE_BLOCK 256 // threads per workgroup of the large-output shape
+#endif
 #ifndef MOE_EP_FP8_GATHER
 #define MOE_EP_FP8_GATHER 2 // ranks per round in the FP8 combine kernels
 #endif
@@ -921,8 +924,8 @@ hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s)
     const int64_t out_bytes = (int64_t)a.P * a.T * a.H * 2;
     const bool wt = out_bytes <= MOE_EP_WT_BYTES;
     if (out_bytes >= MOE_EP_COMBINE_LARGE_BYTES)
-        return wt ? launch_combine_shape<kBlock, MOE_EP_COMBINE_LARGE, true>(a, s)
-                  : launch_combine_shape<kBlock, MOE_EP_COMBINE_LARGE, false>(a, s);
+        return wt ? launch_combine_shape<MOE_EP_COMBINE_LARGE_BLOCK, MOE_EP_COMBINE_LARGE, true>(a, s)
+                  : launch_combine_shape<MOE_EP_COMBINE_LARGE_BLOCK, MOE_EP_COMBINE_LARGE, false>(a, s);
     return wt ? launch_combine_shape<MOE_EP_COMBINE_SMALL_BLOCK, MOE_EP_COMBINE_SMALL, true>(a, s)
               : launch_combine_shape<MOE_EP_COMBINE_SMALL_BLOCK, MOE_EP_COMBINE_SMALL, false>(a, s);
 }
