@@ -228,6 +228,14 @@ FP8 = [
                         H=1056, n_lo=1, n_hi=21, routing="uniform"),
     dataclasses.replace(W.EP8_MXFP8, name="fp8 long rows", P=2, E=8, k=2, T=3, H=8224, n_lo=3, n_hi=3,
                         routing="uniform"),
+    # rows cut into whole workgroup chunks: 448 threads (H = 7168), 64 threads
+    # (H = 5120), 256 threads (H = 4096 * 2)
+    dataclasses.replace(W.EP8_MXFP8, name="fp8 H7168 448-thread chunks", P=3, E=12, k=4, T=9, H=7168,
+                        n_lo=0, n_hi=9, routing="uniform"),
+    dataclasses.replace(W.EP8_MXFP8, name="fp8 H5120 64-thread chunks", P=3, E=12, k=4, T=9, H=5120,
+                        n_lo=0, n_hi=9, routing="uniform"),
+    dataclasses.replace(W.EP8_MXFP8, name="fp8 H8192 256-thread chunks", P=2, E=8, k=3, T=5, H=8192,
+                        n_lo=1, n_hi=5, routing="uniform"),
 ]
 
 
