@@ -41,6 +41,8 @@ def _capture(fn):
     dataclasses.replace(W.EP8_BF16, name="ep8 bf16 graph", H=1024),
     dataclasses.replace(W.EP8_BF16, name="ep8 bf16 long rows graph (write-through stores)", H=7168),
     dataclasses.replace(W.EP8_MXFP8, name="mxfp8 fp8 graph", T=64, H=512, n_lo=10, n_hi=64),
+    dataclasses.replace(W.EP8_MXFP8, name="mxfp8 fp8 graph, 448-thread rows", T=32, H=7168, n_lo=5,
+                        n_hi=32),
 ], ids=lambda w: w.name)
 def test_exchange_graph_replays(w):
     from combine_route_mask_amd.moe_ep import MoeEpExchange
