@@ -91,6 +91,7 @@ constexpr int kScanUnroll = MOE_EP_SCAN_UNROLL; // 256-slot chunks per scan step
 constexpr int kWaves = kBlock / 64;
 constexpr int kPlaneSlots = kBlock;     // slots per id-plane item (one per thread)
 constexpr int kPlaneGroup = 8;          // destinations per id-plane item
+constexpr int64_t kGridCap = 256 * 8 * 64; // most workgroups of a launch (64 rounds of the chip)
 
 // Runs item(w) for the launch's items w < items.  ONE: the grid has one
 // workgroup per item, so a workgroup runs its item and ends; otherwise
@@ -502,7 +503,8 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
     // rows each one runs its item without a loop, so the token's ids come in
     // one scalar load (EP8 dispatch -1%); short rows keep the loop (the
     // one-item form cost the MXFP8 dispatch 2-3%).
-    static_assert(MOE_EP_PREFETCH_ITEMS <= MOE_EP_SCATTER_GRID, "prefetching launches need one workgroup per item");
+    static_assert(MOE_EP_PREFETCH_ITEMS <= MOE_EP_SCATTER_GRID && MOE_EP_PREFETCH_ITEMS <= kGridCap,
+                  "prefetching launches need one workgroup per item");
     constexpr bool one = PF && DV == MOE_EP_DISPATCH_VPT_LONG;
     if constexpr (one) {
         const int64_t w = b - first;
@@ -835,8 +837,7 @@ __global__ __launch_bounds__(BS) void combine_fp8_gather_kernel(CombineArgs a, i
 // resident workgroups); kernels loop over the rest.
 inline int64_t grid_for(int64_t nitems)
 {
-    const int64_t cap = 256 * 8 * 64;
-    return nitems < 1 ? 1 : (nitems < cap ? nitems : cap);
+    return nitems < 1 ? 1 : (nitems < kGridCap ? nitems : kGridCap);
 }
 
 inline int64_t ceil_div(int64_t x, int64_t y) { return (x + y - 1) / y; }
