@@ -330,7 +330,9 @@ class _Flush:
 def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     """Step time of `steps` dispatch+combine steps after `warmup` untimed
     ones, eager (two C-ABI launches per step) and from HIP-graph replays of
-    10 steps each; per-launch kernel times from graphs of 20 back-to-back
+    10 steps each (plus one graph of the remaining steps when `steps` is not
+    a multiple of 10, so exactly `steps` steps are timed); per-launch kernel
+    times from graphs of 20 back-to-back
     launches of one kernel.  With flush_bytes, every timed step and every
     timed single launch follows a write and a read of that many bytes
     (last-level cache cold and clean) and is timed alone.  All events sit on the launch stream."""
@@ -357,10 +359,18 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
                 "dispatch_ms": _time(setup.dispatch, steps) / steps,
                 "combine_ms": _time(setup.combine, steps) / steps, "wall_s": 0.0}
     # one graph holds `per` consecutive steps, so a small step is not bound
-    # by the host's graph-launch rate; `steps` is rounded up to a multiple
-    per = 10
-    replays = -(-steps // per)
+    # by the host's graph-launch rate; a second graph holds the remainder
+    per = min(10, steps)
+    full, rem = divmod(steps, per)
     g_step = _graph(step, per)
+    g_rem = _graph(step, rem) if rem else None
+
+    def timed_steps():
+        for _ in range(full):
+            g_step.replay()
+        if g_rem is not None:
+            g_rem.replay()
+
     for _ in range(max(1, warmup // per)):
         g_step.replay()
     wall0 = time.perf_counter()
@@ -381,7 +391,7 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
         graph_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         del flush
     else:
-        graph_ms = _time(g_step.replay, replays) / (replays * per)
+        graph_ms = _time(timed_steps, 1) / steps
     wall = time.perf_counter() - wall0
     # graph replays must reproduce the eager step bit for bit
     if exchange:
@@ -403,7 +413,7 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
                 ev[i][1].record(stream)
             torch.cuda.synchronize()
             per_kernel.append(float(np.mean([a.elapsed_time(b) for a, b in ev])))
-        del flush, g_step
+        del flush, g_step, g_rem
         return {"ms_per_step": graph_ms, "eager_ms_per_step": eager_ms, "dispatch_ms": per_kernel[0],
                 "combine_ms": per_kernel[1], "wall_s": wall}
     reps = 20
@@ -414,7 +424,7 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     it = max(2, steps // reps)
     disp_ms = _time(g_d.replay, it) / (it * reps)
     comb_ms = _time(g_c.replay, it) / (it * reps)
-    del g_step, g_d, g_c
+    del g_step, g_rem, g_d, g_c
     return {"ms_per_step": graph_ms, "eager_ms_per_step": eager_ms, "dispatch_ms": disp_ms,
             "combine_ms": comb_ms, "wall_s": wall}
 
@@ -608,6 +618,9 @@ def main():
                              WORKLOADS[args.config].name, args.config):
             print(l)
         return
+    if args.steps < 1 or args.warmup < 0:
+        print(json.dumps({"error": "--steps must be >= 1 and --warmup >= 0"}))
+        sys.exit(2)
     if args.gpus != 1:
         print(json.dumps({"error": "this exchange runs P virtual EP ranks on one GPU; "
                                    "--gpus above 1 is not supported"}))
