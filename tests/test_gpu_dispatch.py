@@ -146,6 +146,38 @@ def test_dispatch_empty_ranks_and_T1():
     _run(random_byte_case(w1, 7, counts=[1, 0, 1, 1]))
 
 
+def test_dispatch_and_combine_with_no_tokens():
+    """Every rank sends nothing: every slot carries the marker, counts and
+    offsets are zero, and combine writes no output row; a step after a
+    full one must also clear that step's slots."""
+    w = dataclasses.replace(W.TINY, name="no tokens", P=6, E=24, k=3, T=40, H=1024, n_lo=20, n_hi=40)
+    ex = _run(random_byte_case(w, 31))
+    _run(random_byte_case(w, 32, counts=[0] * w.P), ex=ex)
+    out = torch.full((w.P, w.T, w.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    eo = W.draw_expert_output(w.P, w.T, w.H, 32, device="cuda")
+    ex.combine(eo, out)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()), "combine wrote rows although no rank has tokens"
+
+
+def test_dispatch_with_no_live_rank():
+    """active_rank_mask = 0: nothing is sent or received, no region is
+    written, and combine writes no output row."""
+    w = dataclasses.replace(W.TINY, name="mask 0", T=16, H=256)
+    c = random_byte_case(w, 33)
+    ex = _exchange(w)
+    pl, sc, ids, wt = gpu_inputs(c)
+    ex.workspace.fill_(0x5A)
+    before = ex.workspace.clone()
+    ex.dispatch(pl, ids, wt, scales=sc, num_tokens=c.counts.tolist(), active_rank_mask=0)
+    torch.cuda.synchronize()
+    assert torch.equal(ex.workspace, before), "a masked-off region was written"
+    out = torch.full((w.P, w.T, w.H), 3.0, dtype=torch.bfloat16, device="cuda")
+    ex.combine(W.draw_expert_output(w.P, w.T, w.H, 33, device="cuda"), out)
+    torch.cuda.synchronize()
+    assert bool((out == 3.0).all()), "combine wrote rows of masked-off ranks"
+
+
 def test_dispatch_stale_slots_are_remarked():
     """Two steps on one handle: the second has a smaller T, other counts
     and other routing; every slot of step 2 must reflect step 2 only."""
