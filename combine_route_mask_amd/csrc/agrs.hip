@@ -68,8 +68,8 @@ __global__ __launch_bounds__(kBlock) void allgatherv_kernel(AllGatherArgs a, int
 }
 
 // Ranks whose rows a reduce-scatterv lane loads at once.  P16 AgRs workload,
-// same buffers: 16 -> 169.3 us, 8 -> 171.4, 4 -> 171.3; two vectors per lane
-// instead of one +3% (G 8) / +2% (G 4).
+// same buffers, three buffer placements: 16 and 8 within 0.4% of each other
+// (168.7-169.9 us), 4 the same; two vectors per lane instead of one +2-3%.
 #ifndef MOE_EP_RS_GATHER
 #define MOE_EP_RS_GATHER 16
 #endif
