@@ -3,13 +3,17 @@
 One step = one dispatch + one combine over all P virtual EP ranks of the
 workload, inputs (token rows, ids, weights, expert outputs) resident in
 HBM.  Ten consecutive steps (two launches each) are captured in a HIP
-graph that is replayed until the requested number of steps has run (the
-eager two-launch time is reported beside it).  Prints one JSON line:
+graph, and the remainder in one more, so that exactly the requested number
+of steps is timed (the eager two-launch time is reported beside it).
+Prints one JSON line:
 
   value        tokens/s = N / step time (N = sum of local token counts)
   roofline     the dominant kernel's algorithmic bytes per launch / its
-               average launch time (HIP events on the launch stream),
-               against the MI355X HBM peak (8 TB/s)
+               average launch time (HIP events on the launch stream around
+               a graph of 20 back-to-back launches of it), against the
+               MI355X HBM peak (8 TB/s); traffic: HBM bytes per launch from
+               the committed rocprofv3 counter summary, null when the
+               kernel sources have changed since it was taken
   cpu_baseline the CPU oracle on a bounded sample of the same workload
   also         the other workloads (--also); a '-cold' entry writes 1 GiB
                and reads another 1 GiB before every timed step and launch,
@@ -37,6 +41,8 @@ sys.path.insert(0, ROOT)
 import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+
+
 def traffic_summary_path(config: str) -> str:
     """Committed counter summary of a bench workload (profiles/)."""
     name = "ep8_bf16" if config == "ep8" else config.replace("-", "_")
