@@ -480,6 +480,9 @@ __device__ void scatter_chunk(const DispatchArgs &a, int64_t q, int64_t c)
 //   [0, P)                    receive bookkeeping of destination r
 //   [P, P + plane_blocks)     id / weight planes, (destination group, slot chunk) items
 //   [P + plane_blocks, grid)  payload scatter, (token, row chunk) items
+// except in launches of long rows that do not prefetch, where the id-plane
+// blocks come last (EP64 BF16 dispatch -2%; in prefetching launches the
+// id-plane work then trails the short payload scatter: EP8 / MXFP8 +12%).
 // The last two roles loop over their items when there are more items than
 // blocks.  KQ: id rows of k = 4*KQ ids read as 16-byte vectors (0: any k);
 // DV: 16-byte vectors per thread in a payload row chunk; PF: row loads
@@ -494,16 +497,19 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
         scan_destination<KQ>(a, (int)b);
         return;
     }
-    if (b < a.P + plane_blocks) {
+    constexpr bool plane_last = !PF && DV == MOE_EP_DISPATCH_VPT_LONG;
+    const int64_t npay = (int64_t)gridDim.x - a.P - plane_blocks; // payload blocks
+    const int64_t plane0 = plane_last ? a.P + npay : a.P;         // first id-plane block
+    if (b >= plane0 && b < plane0 + plane_blocks) {
         const int ngroups = (a.P + kPlaneGroup - 1) / kPlaneGroup;
-        for (int64_t w = b - a.P; w < (int64_t)ngroups * nplane; w += plane_blocks) {
+        for (int64_t w = b - plane0; w < (int64_t)ngroups * nplane; w += plane_blocks) {
             const int g = (int)(w / nplane);
             write_id_planes<KQ>(a, g * kPlaneGroup, min(a.P, (g + 1) * kPlaneGroup), w % nplane);
         }
         return;
     }
     const int64_t S = (int64_t)a.P * a.T;
-    const int64_t first = a.P + plane_blocks;
+    const int64_t first = plane_last ? a.P : a.P + plane_blocks; // first payload block
     // A prefetching launch has a workgroup for every payload item.  With long
     // rows each one runs its item without a loop, so the token's ids come in
     // one scalar load (EP8 dispatch -1%); short rows keep the loop (the
@@ -517,8 +523,7 @@ __global__ __launch_bounds__(kBlock) void dispatch_kernel(DispatchArgs a, int64_
             scatter_chunk<KQ, DV, PF, WT, XF>(a, w / nchunk, w % nchunk);
         return;
     }
-    const int64_t stride = (int64_t)gridDim.x - first;
-    for (int64_t w = b - first; w < S * nchunk; w += stride)
+    for (int64_t w = b - first; w < S * nchunk; w += npay)
         scatter_chunk<KQ, DV, PF, WT, XF>(a, w / nchunk, w % nchunk);
 }
 
