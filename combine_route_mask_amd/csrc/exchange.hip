@@ -871,18 +871,29 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
 {
     const int64_t S = (int64_t)a.P * a.T;
     const int64_t nplane = ceil_div(S, kPlaneSlots);
-    const int64_t plane_blocks = grid_for(ceil_div(a.P, kPlaneGroup) * nplane);
+    int64_t plane_blocks = grid_for(ceil_div(a.P, kPlaneGroup) * nplane);
     const bool long_rows = a.row_bytes >= MOE_EP_DISPATCH_LONG_ROW;
     const int dv = long_rows ? MOE_EP_DISPATCH_VPT_LONG : MOE_EP_DISPATCH_VPT_SHORT;
     const int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
-    const int64_t grid =
-        a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
     const bool pf = S * nchunk <= MOE_EP_PREFETCH_ITEMS;
-    // write-through payload stores: long rows only, and a bound on the
-    // payload bytes written (each token goes to at most min(P, k) ranks)
     int64_t N = 0;
     for (int i = 0; i < a.P; ++i)
         N += a.n[i];
+    // Short-row launches that do not prefetch run their id-plane blocks
+    // first.  When the id planes are a small share of the launch's bytes,
+    // fewer such blocks (each looping over several items) leave the early
+    // slots to the payload scatter: EP64 NVFP4 dispatch -6% with 128 or 64
+    // blocks instead of 1024; with 32 the id planes become the straggler.
+    if (!pf && !long_rows) {
+        const int64_t plane_bytes = S * a.P * 4 * a.k;
+        const int64_t payload_bytes = N * std::min(a.P, a.k) * (a.row_bytes + a.srow_bytes);
+        if (plane_bytes * 10 < payload_bytes)
+            plane_blocks = std::min<int64_t>(plane_blocks, 128);
+    }
+    const int64_t grid =
+        a.P + plane_blocks + std::min<int64_t>(grid_for(S * nchunk), MOE_EP_SCATTER_GRID);
+    // write-through payload stores: long rows only, and a bound on the
+    // payload bytes written (each token goes to at most min(P, k) ranks)
     const bool wt = long_rows && N * std::min(a.P, a.k) * a.row_bytes <= MOE_EP_WT_BYTES;
     // extra rows that fit one word per lane travel with the payload loads
     const bool xf = side_row_fits(a.extra, a.xrow_bytes, a.off_extra, a.region);
