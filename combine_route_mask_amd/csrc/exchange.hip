@@ -612,7 +612,8 @@ __device__ __forceinline__ void combine_bf16_item(const CombineArgs &a, int64_t 
 template <int BS, int VPT, int G, bool WT, bool ONE>
 __global__ __launch_bounds__(BS) void combine_bf16_kernel(CombineArgs a, int64_t nchunk)
 {
-    for_each_item<ONE>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { combine_bf16_item<BS, VPT, G, WT>(a, w, nchunk); });
+    for_each_item<ONE>((int64_t)a.P * a.T * nchunk,
+                       [&](int64_t w) { combine_bf16_item<BS, VPT, G, WT>(a, w, nchunk); });
 }
 
 // e4m3 codes (two words, element 0 in the lowest byte) and e8m0 scale code
@@ -659,9 +660,10 @@ __device__ __forceinline__ void quantise8(u32x4 x, uint32_t &c0, uint32_t &c1, u
 }
 
 // FP8 combine, sending side: item (token q = s*T + t, chunk c of BS * 16
-// elements, BS threads per workgroup).  Every rank r that holds the token quantises its row q (e4m3fn,
-// one e8m0 scale per 32 elements) into source rank s's landing plane at slot
-// r*T + t; the rows of up to G ranks are loaded before any is quantised.
+// elements, BS threads per workgroup).  Every rank r that holds the token
+// quantises its row q (e4m3fn, one e8m0 scale per 32 elements) into source
+// rank s's landing plane at slot r*T + t; the rows of up to G ranks are
+// loaded before any is quantised.
 // Each lane owns 8 elements in each half of the chunk (elements
 // c*BS*16 + h*BS*8 + lane*8 ..), so every load instruction of a wave covers
 // 1 KB of a row without gaps; four lanes share a block.  WT: the codes are
@@ -734,7 +736,8 @@ __device__ __forceinline__ void fp8_quant_item(const CombineArgs &a, int64_t w, 
 template <int BS, int G, bool WT>
 __global__ __launch_bounds__(BS) void combine_fp8_quant_kernel(CombineArgs a, int64_t nchunk)
 {
-    for_each_item<false>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { fp8_quant_item<BS, G, WT>(a, w, nchunk); });
+    for_each_item<false>((int64_t)a.P * a.T * nchunk,
+                         [&](int64_t w) { fp8_quant_item<BS, G, WT>(a, w, nchunk); });
 }
 
 // FP8 combine, receiving side: item (token q = s*T + t, chunk c of BS * 16
@@ -840,7 +843,8 @@ __device__ __forceinline__ void fp8_gather_item(const CombineArgs &a, int64_t w,
 template <int BS, int G>
 __global__ __launch_bounds__(BS) void combine_fp8_gather_kernel(CombineArgs a, int64_t nchunk)
 {
-    for_each_item<false>((int64_t)a.P * a.T * nchunk, [&](int64_t w) { fp8_gather_item<BS, G>(a, w, nchunk); });
+    for_each_item<false>((int64_t)a.P * a.T * nchunk,
+                         [&](int64_t w) { fp8_gather_item<BS, G>(a, w, nchunk); });
 }
 
 // Grid of nitems workgroups capped at 64 rounds of the chip (256 CUs x 8
