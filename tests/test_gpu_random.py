@@ -9,7 +9,9 @@ dequantised terms).
 Drawn per case: P in 1..64, experts per rank 1..8 (E % 4 == 0), top_k up
 to 16 with duplicate and out-of-range ids, T and per-rank counts, the
 dispatch format (BF16 / MXFP8 / NVFP4 / DeepSeekFp8) and combine format,
-hidden sizes that leave ragged 256-lane chunks, weights present or not,
+hidden sizes that leave ragged 256-lane chunks (and, in 24 more cases,
+rows of 1024..14336 elements for every combine workgroup shape), weights
+present or not,
 the invalid expert id, an active rank mask, extra payload bytes and EPLB
 statistics.  Masked-off regions and output rows must stay untouched."""
 import dataclasses
@@ -44,22 +46,27 @@ class Case:
                 f"{f'-eplb{self.n_eplb}' if self.n_eplb else ''}-s{w.seed}")
 
 
-def _cases(n=120, seed=20261202):
+def _cases(n=120, seed=20261202, wide=False):
+    """wide: few ranks and tokens but rows of 1024..14336 elements, so the
+    combine kernels take every workgroup shape they choose by row width."""
     rng = np.random.default_rng(seed)
     out = []
     while len(out) < n:
-        P = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24, 32, 48, 64]))
+        P = int(rng.choice([1, 2, 3, 4, 5, 6, 7, 8, 12, 16, 24, 32, 48, 64] if not wide else [1, 2, 3, 4, 6, 8]))
         E = P * int(rng.choice([1, 2, 3, 4, 5, 8]))
         if E % 4:
             continue
         k = int(rng.integers(1, min(E, 12) + 1)) if rng.random() < 0.85 else min(E, 16)
-        T = int(rng.integers(1, 41)) if P <= 16 else int(rng.integers(1, 9))
+        T = int(rng.integers(1, 41)) if P <= 16 and not wide else int(rng.integers(1, 9))
         fmt = str(rng.choice(["bf16", "bf16", "mxfp8", "nvfp4", "deepseek_fp8"]))
-        comb = "fp8" if rng.random() < 0.3 else "bf16"
+        comb = "fp8" if rng.random() < (0.3 if not wide else 0.6) else "bf16"
         quantum = {"bf16": 8, "mxfp8": 32, "nvfp4": 32, "deepseek_fp8": 128}[fmt]
         if comb == "fp8":
             quantum = max(quantum, 32)
-        H = quantum * int(rng.integers(1, max(2, 720 // quantum) + 1))
+        if wide:
+            H = int(rng.choice([1024, 2048, 3072, 5120, 7168, 8192, 14336, 7168 + 1024]))
+        else:
+            H = quantum * int(rng.integers(1, max(2, 720 // quantum) + 1))
         alive = tuple(range(P))
         if P > 1 and rng.random() < 0.3:
             alive = tuple(sorted(rng.choice(P, size=int(rng.integers(1, P + 1)), replace=False).tolist()))
@@ -72,7 +79,7 @@ def _cases(n=120, seed=20261202):
     return out
 
 
-CASES = _cases()
+CASES = _cases() + _cases(n=24, seed=20261203, wide=True)
 
 
 @pytest.fixture(scope="module", autouse=True)
