@@ -4,10 +4,13 @@ TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the
 benchmark's CPU-baseline leg are the only callers.  The product path (the
 HIP library and its binding) never imports this package.
 
-The arithmetic lives in ``moe_ep_oracle.c`` (plain single-threaded C,
-double-precision sums); this module compiles it with gcc on first use and
-wraps it with numpy arrays.  See the C file's header for the definitions
-and the pages each one follows.
+The arithmetic lives in ``moe_ep_oracle.c`` (plain single-threaded C);
+this module compiles it with gcc on first use and wraps it with numpy
+arrays.  See the C file's header for the definitions and the pages each
+one follows.  Every sum over ranks comes back twice: ``ref``, the fp32 sum
+in ascending rank order from +0 (the reference the combine tolerance is
+stated against; ``y`` is ``ref`` rounded to bf16), and ``exact``, the same
+sum in double (exact for sums of bf16 or e4m3 terms).
 
 Parity status: every function here is pinned by the CPU tests
 (brute force on tiny inputs, closed forms, invariants, library codecs and
@@ -15,6 +18,7 @@ hand-worked golden cases under ``tests/golden``); none is unpinned.
 """
 from __future__ import annotations
 
+import collections
 import ctypes as C
 import os
 import subprocess
@@ -33,8 +37,10 @@ def build(force: bool = False) -> str:
     """Compile the oracle with gcc (-O2, no threads, no vector intrinsics)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
-        subprocess.check_call(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-Wall",
-                               "-Wextra", "-o", tmp, _SRC, "-lm"])
+        # ISO C11 with SSE arithmetic: float operations round to single
+        # precision one by one (no contraction, no excess precision)
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared",
+                               "-Wall", "-Wextra", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -75,20 +81,21 @@ def _declare(L):
     L.orc_dispatch.argtypes = [_i, _i, _i, _i, C.c_int32, C.c_uint64, _p, _p, _i64, _p, _i64,
                                _p, _i64, _p, _p, _i, _i, _p, _p, _p, _p, _p, _p, _p, _p]
     L.orc_dispatch.restype = None
-    L.orc_combine_token_bf16.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _p, _p]
+    L.orc_combine_token_bf16.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _i64, _p, _p, _p]
     L.orc_combine_token_bf16.restype = None
-    L.orc_combine_bf16.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i, _i, _p, _p, _p]
+    L.orc_combine_bf16.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i64, _i64, _i, _i,
+                                   _p, _p, _p]
     L.orc_combine_bf16.restype = None
-    L.orc_combine_token_fp8.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _p, _p, _p, _p]
+    L.orc_combine_token_fp8.argtypes = [_i, _i, _i, _i, C.c_uint64, _p, _p, _i64, _p, _p, _p, _p, _p]
     L.orc_combine_token_fp8.restype = None
-    L.orc_combine_fp8.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i, _i, _p, _p, _p,
-                                  _p, _p, _p, _p]
+    L.orc_combine_fp8.argtypes = [_i, _i, _i, _i, _i, C.c_uint64, _p, _p, _p, _i64, _i64, _i, _i,
+                                  _p, _p, _p, _p, _p, _p, _p]
     L.orc_combine_fp8.restype = None
     L.orc_eplb_allgather.argtypes = [_i, _i, C.c_uint64, _p, _i, _p]
     L.orc_eplb_allgather.restype = None
     L.orc_allgatherv.argtypes = [_i, _p, _i64, _p, _i64, _p]
     L.orc_allgatherv.restype = None
-    L.orc_reduce_scatterv.argtypes = [_i, _p, _i, _p, _i, _p, _p]
+    L.orc_reduce_scatterv.argtypes = [_i, _p, _i, _p, _i, _p, _p, _p]
     L.orc_reduce_scatterv.restype = None
     return L
 
@@ -201,71 +208,99 @@ def eplb_allgather(stats, r: int, active=None, out=None):
     return out
 
 
-def combine_token_bf16(ids_row, eo_rows, *, E: int, active=None):
+# Results of the sums over ranks: ref is the fp32 sum in ascending rank
+# order from +0 (float32), y / out its bf16 rounding (uint16 bit patterns),
+# exact the same sum in double.
+BF16Combine = collections.namedtuple("BF16Combine", "ref y exact")
+FP8Combine = collections.namedtuple("FP8Combine", "land_codes land_scales ref y exact")
+TokenFP8 = collections.namedtuple("TokenFP8", "codes scales ref y exact")
+ReduceScatter = collections.namedtuple("ReduceScatter", "ref out exact")
+
+
+def combine_token_bf16(ids_row, eo_rows, *, E: int, active=None) -> BF16Combine:
     """One token: eo_rows uint16 [P, H] (its slot's row on every rank)."""
     ids_row = _c(ids_row, np.int32)
     eo_rows = _c(eo_rows, np.uint16)
     P, H = eo_rows.shape
-    ref = np.zeros(H, np.float64)
+    ref = np.zeros(H, np.float32)
+    exact = np.zeros(H, np.float64)
     y = np.zeros(H, np.uint16)
     lib().orc_combine_token_bf16(P, H, ids_row.shape[0], E, _active(active, P), _ptr(ids_row),
-                                 _ptr(eo_rows), _ptr(ref), _ptr(y))
-    return ref, y
+                                 _ptr(eo_rows), H, _ptr(ref), _ptr(exact), _ptr(y))
+    return BF16Combine(ref, y, exact)
 
 
-def combine_bf16(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None):
-    """BF16 combine of source ranks s0..s1-1; eo uint16 [P, P*T, H].
-    Returns (ref float64 [n, T, H], y uint16 [n, T, H]); rows t >= n_s
-    stay zero."""
+def _eo_range(eo, P, T, s0, s1, slot0):
+    """Checks that eo [P, nslot, H] (slots slot0 .. slot0 + nslot - 1)
+    holds every slot of sources s0 .. s1-1."""
+    assert eo.ndim == 3 and eo.shape[0] == P, "eo must be [P, slots, H]"
+    nslot = eo.shape[1]
+    assert slot0 <= s0 * T and s1 * T <= slot0 + nslot, "eo does not hold the sources' slots"
+    return nslot
+
+
+def combine_bf16(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None,
+                 slot0: int = 0) -> BF16Combine:
+    """BF16 combine of source ranks s0..s1-1.  eo: uint16 [P, nslot, H],
+    every rank's expert output for slots slot0 .. slot0 + nslot - 1 (the
+    whole [P, P*T, H] tensor by default).  Returns ref float32, y uint16,
+    exact float64, each [s1-s0, T, H]; rows t >= n_s stay zero."""
     counts = _c(counts, np.int32)
     ids = _c(ids, np.int32)
     eo = _c(eo, np.uint16)
     P, T, k = ids.shape
     H = eo.shape[-1]
     s1 = P if s1 is None else s1
-    ref = np.zeros((s1 - s0, T, H), np.float64)
+    nslot = _eo_range(eo, P, T, s0, s1, slot0)
+    ref = np.zeros((s1 - s0, T, H), np.float32)
+    exact = np.zeros((s1 - s0, T, H), np.float64)
     y = np.zeros((s1 - s0, T, H), np.uint16)
-    scratch = np.zeros((P, H), np.uint16)
     lib().orc_combine_bf16(P, T, H, k, E, _active(active, P), _ptr(counts), _ptr(ids), _ptr(eo),
-                           s0, s1, _ptr(ref), _ptr(y), _ptr(scratch))
-    return ref, y
+                           slot0, nslot, s0, s1, _ptr(ref), _ptr(exact), _ptr(y))
+    return BF16Combine(ref, y, exact)
 
 
-def combine_token_fp8(ids_row, eo_rows, *, E: int, active=None):
+def combine_token_fp8(ids_row, eo_rows, *, E: int, active=None) -> TokenFP8:
+    """One token's FP8 combine: codes [P, H], scales [P, H/32] (rows of
+    ranks the token went to), ref float32, y uint16, exact float64 [H]."""
     ids_row = _c(ids_row, np.int32)
     eo_rows = _c(eo_rows, np.uint16)
     P, H = eo_rows.shape
     codes = np.zeros((P, H), np.uint8)
     scales = np.zeros((P, H // 32), np.uint8)
-    ref = np.zeros(H, np.float64)
+    ref = np.zeros(H, np.float32)
+    exact = np.zeros(H, np.float64)
     y = np.zeros(H, np.uint16)
     lib().orc_combine_token_fp8(P, H, ids_row.shape[0], E, _active(active, P), _ptr(ids_row),
-                                _ptr(eo_rows), _ptr(codes), _ptr(scales), _ptr(ref), _ptr(y))
-    return codes, scales, ref, y
+                                _ptr(eo_rows), H, _ptr(codes), _ptr(scales), _ptr(ref),
+                                _ptr(exact), _ptr(y))
+    return TokenFP8(codes, scales, ref, y, exact)
 
 
-def combine_fp8(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None):
-    """FP8 combine of source ranks s0..s1-1.  Returns (land_codes
-    [n, P*T, H], land_scales [n, P*T, H/32], ref_q [n, T, H] float64,
-    y [n, T, H] uint16)."""
+def combine_fp8(counts, ids, eo, *, E: int, s0: int = 0, s1=None, active=None,
+                slot0: int = 0) -> FP8Combine:
+    """FP8 combine of source ranks s0..s1-1 (eo as for combine_bf16).
+    Returns land_codes [n, P*T, H], land_scales [n, P*T, H/32] (uint8),
+    ref float32, y uint16 and exact float64, each [n, T, H]."""
     counts = _c(counts, np.int32)
     ids = _c(ids, np.int32)
     eo = _c(eo, np.uint16)
     P, T, k = ids.shape
     H = eo.shape[-1]
     s1 = P if s1 is None else s1
+    nslot = _eo_range(eo, P, T, s0, s1, slot0)
     n = s1 - s0
     land_codes = np.zeros((n, P * T, H), np.uint8)
     land_scales = np.zeros((n, P * T, H // 32), np.uint8)
-    ref = np.zeros((n, T, H), np.float64)
+    ref = np.zeros((n, T, H), np.float32)
+    exact = np.zeros((n, T, H), np.float64)
     y = np.zeros((n, T, H), np.uint16)
-    sr = np.zeros((P, H), np.uint16)
     sc = np.zeros((P, H), np.uint8)
     ss = np.zeros((P, H // 32), np.uint8)
     lib().orc_combine_fp8(P, T, H, k, E, _active(active, P), _ptr(counts), _ptr(ids), _ptr(eo),
-                          s0, s1, _ptr(land_codes), _ptr(land_scales), _ptr(ref), _ptr(y),
-                          _ptr(sr), _ptr(sc), _ptr(ss))
-    return land_codes, land_scales, ref, y
+                          slot0, nslot, s0, s1, _ptr(land_codes), _ptr(land_scales), _ptr(ref),
+                          _ptr(exact), _ptr(y), _ptr(sc), _ptr(ss))
+    return FP8Combine(land_codes, land_scales, ref, y, exact)
 
 
 def allgatherv(sizes, rows):
@@ -279,13 +314,15 @@ def allgatherv(sizes, rows):
     return out
 
 
-def reduce_scatterv(sizes, partial, r: int):
-    """partial: uint16 [P, sum(sizes), H].  Returns (ref float64, out
-    uint16), both [sizes[r], H]."""
+def reduce_scatterv(sizes, partial, r: int) -> ReduceScatter:
+    """partial: uint16 [P, sum(sizes), H].  Returns ref float32, out
+    uint16 and exact float64, each [sizes[r], H]."""
     sizes = _c(sizes, np.int32)
     partial = _c(partial, np.uint16)
     P, total, H = partial.shape
-    ref = np.zeros((int(sizes[r]), H), np.float64)
+    ref = np.zeros((int(sizes[r]), H), np.float32)
+    exact = np.zeros((int(sizes[r]), H), np.float64)
     out = np.zeros((int(sizes[r]), H), np.uint16)
-    lib().orc_reduce_scatterv(P, _ptr(sizes), H, _ptr(partial), r, _ptr(ref), _ptr(out))
-    return ref, out
+    lib().orc_reduce_scatterv(P, _ptr(sizes), H, _ptr(partial), r, _ptr(ref), _ptr(exact),
+                              _ptr(out))
+    return ReduceScatter(ref, out, exact)

@@ -7,7 +7,12 @@
  * HIP library) never calls it and shares no code with it.
  *
  * Plain, slow, single-threaded C.  Every result is written out from its
- * definition; floating-point sums are taken in double precision.
+ * definition.  Every sum over ranks is taken twice: in single precision
+ * (float), adding the terms one by one in ascending rank order starting
+ * from +0 -- the fp32 reference the combine's tolerance is stated against,
+ * and the value the bf16 results are rounded from -- and in double
+ * precision, which holds every sum of bf16 or e4m3 terms exactly and
+ * serves the error-bound checks.
  *
  * Sources (FlashInfer and vLLM API documentation pages):
  *  - FlashInfer "flashinfer.moe_ep.NVLinkTwoSidedAlltoAll", dispatch():
@@ -40,6 +45,7 @@
  *  - a token goes to a rank once, however many of its experts live there;
  *  - every slot that receives no row carries invalid_id in all k id
  *    entries, not only the slots past a source's token count;
+ *  - sums over ranks are fp32, in ascending rank order from +0;
  *  - output rounding is round-to-nearest-even to bf16;
  *  - extra per-token payload bytes (FlashInfer "NVLinkOneSidedConfig",
  *    options paragraph, extra_payload_bytes_per_token) travel with the
@@ -327,99 +333,111 @@ void orc_eplb_allgather(int P, int n, uint64_t active, const int32_t *stats, int
 /* ------------------------------------------------------------------ */
 
 /*
- * One token's BF16 combine.  eo_rows [P][H] holds, for every rank r, the
- * row rank r's expert computation produced in this token's slot
- * (whatever it holds where the token was not sent).  ref[H] is the exact
- * sum (double) over ranks r that own one of the token's experts, in
- * ascending r; y[H] is ref rounded to bf16.  A token sent nowhere gives
- * +0.  Ranks whose bit in active is clear contribute nothing.
+ * One token's BF16 combine.  Rank r's row for this token's slot is
+ * eo_row0 + r * rank_stride (elements): whatever that rank's expert
+ * computation wrote there, read only when the token was sent to r.  ref[H]
+ * is the fp32 sum over ranks r that own one of the token's experts, added
+ * in ascending r starting from +0; exact[H] is the same sum in double
+ * (exact for up to 2^20 bf16 terms); y[H] is ref rounded to bf16.  A token
+ * sent nowhere gives +0.  Ranks whose bit in active is clear contribute
+ * nothing.
  */
 void orc_combine_token_bf16(int P, int H, int k, int E, uint64_t active, const int32_t *ids_row,
-                            const uint16_t *eo_rows, double *ref, uint16_t *y)
+                            const uint16_t *eo_row0, int64_t rank_stride,
+                            float *ref, double *exact, uint16_t *y)
 {
-    for (int h = 0; h < H; ++h)
-        ref[h] = 0.0;
+    for (int h = 0; h < H; ++h) {
+        ref[h] = 0.0f;
+        exact[h] = 0.0;
+    }
     for (int r = 0; r < P; ++r) {
         if (!live(active, r) || !orc_token_goes_to(ids_row, k, E, P, r))
             continue;
-        for (int h = 0; h < H; ++h)
-            ref[h] += orc_bf16_to_double(eo_rows[(int64_t)r * H + h]);
+        const uint16_t *row = eo_row0 + (int64_t)r * rank_stride;
+        for (int h = 0; h < H; ++h) {
+            double v = orc_bf16_to_double(row[h]);
+            ref[h] = ref[h] + (float)v;
+            exact[h] += v;
+        }
     }
     for (int h = 0; h < H; ++h)
-        y[h] = orc_double_to_bf16(ref[h]);
+        y[h] = orc_double_to_bf16((double)ref[h]);
 }
 
 /*
- * BF16 combine for source ranks s in [s0, s1): eo [P][P*T][H] is every
- * rank's expert output by slot, ref / y are [s1-s0][T][H]; rows t >= n_s
- * are left untouched (the result holds local_num_tokens rows), and so are
- * all rows of a source whose bit in active is clear.
+ * BF16 combine for source ranks s in [s0, s1).  eo holds every rank's
+ * expert output for slots slot0 .. slot0 + nslot - 1 ([P][nslot][H]; the
+ * whole tensor [P][P*T][H] when slot0 = 0 and nslot = P*T); the slots of
+ * the sources s0 .. s1-1 must lie in that range.  ref / exact / y are
+ * [s1-s0][T][H]; rows t >= n_s are left untouched (the result holds
+ * local_num_tokens rows), and so are all rows of a source whose bit in
+ * active is clear.
  */
 void orc_combine_bf16(int P, int T, int H, int k, int E, uint64_t active, const int32_t *counts,
-                      const int32_t *ids, const uint16_t *eo, int s0, int s1,
-                      double *ref, uint16_t *y, uint16_t *scratch_rows /* [P][H] */)
+                      const int32_t *ids, const uint16_t *eo, int64_t slot0, int64_t nslot,
+                      int s0, int s1, float *ref, double *exact, uint16_t *y)
 {
-    int64_t slots = (int64_t)P * T;
     for (int s = s0; s < s1; ++s)
         for (int t = 0; live(active, s) && t < counts[s]; ++t) {
             int64_t q = (int64_t)s * T + t;
-            for (int r = 0; r < P; ++r)
-                memcpy(scratch_rows + (int64_t)r * H, eo + ((int64_t)r * slots + q) * H,
-                       sizeof(uint16_t) * (size_t)H);
             int64_t o = ((int64_t)(s - s0) * T + t) * H;
-            orc_combine_token_bf16(P, H, k, E, active, ids + q * k, scratch_rows, ref + o, y + o);
+            orc_combine_token_bf16(P, H, k, E, active, ids + q * k, eo + (q - slot0) * H, nslot * H,
+                                   ref + o, exact + o, y + o);
         }
 }
 
 /*
  * One token's FP8 combine.  Each owning rank r quantises its row
- * eo_rows[r] (codes[r], scales[r]); the token's result is the exact sum
- * of the dequantised rows in ascending r (ref_q), rounded to bf16 (y).
- * Rows of ranks the token was not sent to are left untouched in codes /
- * scales.
+ * (eo_row0 + r * rank_stride) into codes[r] / scales[r] ([P][H] and
+ * [P][H/32]); the token's result is the fp32 sum of the dequantised rows,
+ * added in ascending r from +0 (ref_q), rounded to bf16 (y); exact_q is
+ * the same sum in double.  Rows of ranks the token was not sent to are
+ * left untouched in codes / scales.
  */
 void orc_combine_token_fp8(int P, int H, int k, int E, uint64_t active, const int32_t *ids_row,
-                           const uint16_t *eo_rows, uint8_t *codes, uint8_t *scales,
-                           double *ref_q, uint16_t *y)
+                           const uint16_t *eo_row0, int64_t rank_stride, uint8_t *codes,
+                           uint8_t *scales, float *ref_q, double *exact_q, uint16_t *y)
 {
-    for (int h = 0; h < H; ++h)
-        ref_q[h] = 0.0;
+    for (int h = 0; h < H; ++h) {
+        ref_q[h] = 0.0f;
+        exact_q[h] = 0.0;
+    }
     for (int r = 0; r < P; ++r) {
         if (!live(active, r) || !orc_token_goes_to(ids_row, k, E, P, r))
             continue;
         uint8_t *c = codes + (int64_t)r * H;
         uint8_t *sc = scales + (int64_t)r * (H / 32);
-        orc_fp8_quantize_row(H, eo_rows + (int64_t)r * H, c, sc);
-        for (int h = 0; h < H; ++h)
-            ref_q[h] += orc_fp8_dequant(c[h], sc[h / 32]);
+        orc_fp8_quantize_row(H, eo_row0 + (int64_t)r * rank_stride, c, sc);
+        for (int h = 0; h < H; ++h) {
+            double v = orc_fp8_dequant(c[h], sc[h / 32]);
+            ref_q[h] = ref_q[h] + (float)v;
+            exact_q[h] += v;
+        }
     }
     for (int h = 0; h < H; ++h)
-        y[h] = orc_double_to_bf16(ref_q[h]);
+        y[h] = orc_double_to_bf16((double)ref_q[h]);
 }
 
 /*
- * FP8 combine for source ranks s in [s0, s1).  The quantised rows a
- * source rank s receives land, one per sending rank r, at slot
- * r * T + t of s's landing planes: land_codes [s1-s0][P*T][H],
+ * FP8 combine for source ranks s in [s0, s1); eo as for orc_combine_bf16.
+ * The quantised rows a source rank s receives land, one per sending rank
+ * r, at slot r * T + t of s's landing planes: land_codes [s1-s0][P*T][H],
  * land_scales [s1-s0][P*T][H/32] (slots with no row are untouched).
- * ref_q / y are [s1-s0][T][H].
+ * ref_q / exact_q / y are [s1-s0][T][H].
  */
 void orc_combine_fp8(int P, int T, int H, int k, int E, uint64_t active, const int32_t *counts,
-                     const int32_t *ids, const uint16_t *eo, int s0, int s1,
-                     uint8_t *land_codes, uint8_t *land_scales, double *ref_q, uint16_t *y,
-                     uint16_t *scratch_rows /* [P][H] */,
+                     const int32_t *ids, const uint16_t *eo, int64_t slot0, int64_t nslot,
+                     int s0, int s1, uint8_t *land_codes, uint8_t *land_scales, float *ref_q,
+                     double *exact_q, uint16_t *y,
                      uint8_t *scratch_codes /* [P][H] */, uint8_t *scratch_scales /* [P][H/32] */)
 {
     int64_t slots = (int64_t)P * T;
     for (int s = s0; s < s1; ++s)
         for (int t = 0; live(active, s) && t < counts[s]; ++t) {
             int64_t q = (int64_t)s * T + t;
-            for (int r = 0; r < P; ++r)
-                memcpy(scratch_rows + (int64_t)r * H, eo + ((int64_t)r * slots + q) * H,
-                       sizeof(uint16_t) * (size_t)H);
             int64_t o = ((int64_t)(s - s0) * T + t) * H;
-            orc_combine_token_fp8(P, H, k, E, active, ids + q * k, scratch_rows, scratch_codes,
-                                  scratch_scales, ref_q + o, y + o);
+            orc_combine_token_fp8(P, H, k, E, active, ids + q * k, eo + (q - slot0) * H, nslot * H,
+                                  scratch_codes, scratch_scales, ref_q + o, exact_q + o, y + o);
             for (int r = 0; r < P; ++r) {
                 if (!live(active, r) || !orc_token_goes_to(ids + q * k, k, E, P, r))
                     continue;
@@ -456,11 +474,12 @@ void orc_allgatherv(int P, const int32_t *sizes, int64_t row_bytes,
 /*
  * reduce_scatterv along dim 0 for rank r: in [P][sum(sizes)][H] bf16 is
  * every rank's full-length partial; rank r keeps rows off_r .. off_r +
- * sizes[r] - 1 summed over ranks (ascending q, double), off_r being the
- * sum of sizes[q] for q < r.  ref / out are [sizes[r]][H].
+ * sizes[r] - 1 summed over ranks, off_r being the sum of sizes[q] for
+ * q < r.  ref is the fp32 sum (ascending q, from +0), exact the same sum
+ * in double, out = ref rounded to bf16; all three are [sizes[r]][H].
  */
 void orc_reduce_scatterv(int P, const int32_t *sizes, int H, const uint16_t *in,
-                         int r, double *ref, uint16_t *out)
+                         int r, float *ref, double *exact, uint16_t *out)
 {
     int64_t total = 0, off = 0;
     for (int q = 0; q < P; ++q) {
@@ -470,10 +489,15 @@ void orc_reduce_scatterv(int P, const int32_t *sizes, int H, const uint16_t *in,
     }
     for (int32_t i = 0; i < sizes[r]; ++i)
         for (int h = 0; h < H; ++h) {
-            double acc = 0.0;
-            for (int q = 0; q < P; ++q)
-                acc += orc_bf16_to_double(in[((int64_t)q * total + off + i) * H + h]);
+            float acc = 0.0f;
+            double ex = 0.0;
+            for (int q = 0; q < P; ++q) {
+                double v = orc_bf16_to_double(in[((int64_t)q * total + off + i) * H + h]);
+                acc = acc + (float)v;
+                ex += v;
+            }
             ref[(int64_t)i * H + h] = acc;
-            out[(int64_t)i * H + h] = orc_double_to_bf16(acc);
+            exact[(int64_t)i * H + h] = ex;
+            out[(int64_t)i * H + h] = orc_double_to_bf16((double)acc);
         }
 }

@@ -81,3 +81,44 @@ def combine_bf16(counts, ids, eo_bits, E, alive=None):
                     acc[h] += float(v)
             out[(s, t)] = acc
     return out
+
+
+def combine_bf16_fp32(counts, ids, eo_bits, E, alive=None):
+    """The same push-style walk summing in single precision: numpy float32
+    additions one rank at a time, ascending r, from +0.  Returns
+    {(s, t): float32 array}."""
+    P, T, k = ids.shape
+    epr = E // P
+    alive = set(range(P)) if alive is None else set(alive)
+    out = {}
+    for s in range(P):
+        if s not in alive:
+            continue
+        for t in range(int(counts[s])):
+            dests = sorted({int(e) // epr for e in ids[s][t] if 0 <= int(e) < E} & alive)
+            acc = np.zeros(eo_bits.shape[-1], np.float32)
+            for r in dests:
+                acc = (acc + _bf16_bits_to_float(eo_bits[r, s * T + t]).astype(np.float32)).astype(np.float32)
+            out[(s, t)] = acc
+    return out
+
+
+def fp8_dequantise(codes, scales):
+    """Values of e4m3 codes [..., H] with one e8m0 scale per 32 elements
+    [..., H/32] (torch's float8_e4m3fn decode times 2^(scale - 127); a
+    scale of 0xFF is NaN), float64."""
+    c = torch.from_numpy(np.ascontiguousarray(codes, np.uint8)).view(torch.float8_e4m3fn).double()
+    sc = np.asarray(scales, np.int64)
+    mult = np.where(sc == 0xFF, np.nan, np.ldexp(1.0, sc - 127))
+    return c.numpy() * np.repeat(mult, 32, axis=-1)
+
+
+def reduce_scatterv_fp32(sizes, partial_bits, r):
+    """Rank r's rows of the reduce-scatterv: float32 sums of every rank's
+    partial row, ascending rank, from +0."""
+    P = len(sizes)
+    off = sum(int(sizes[q]) for q in range(r))
+    acc = np.zeros((int(sizes[r]), partial_bits.shape[-1]), np.float32)
+    for q in range(P):
+        acc = (acc + _bf16_bits_to_float(partial_bits[q, off:off + int(sizes[r])]).astype(np.float32)).astype(np.float32)
+    return acc

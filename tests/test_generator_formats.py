@@ -10,6 +10,7 @@ DeepSeekFp8 workloads something else).
   in test_oracle_codecs.py); nearest-value checks here are brute force
   over every code."""
 import numpy as np
+import pytest
 import torch
 
 import workloads as W
@@ -87,3 +88,36 @@ def test_deepseek_fp8_scale_and_elements():
     y = (torch.from_numpy(xf) / torch.from_numpy(sc)[..., None]).numpy()
     best = np.nanmin(np.abs(E4M3_FINITE[None, :] - y.reshape(-1, 1)), axis=1).reshape(y.shape)
     assert np.all(np.abs(dec - y) <= best)
+
+
+def test_zipf_routing_is_popularity_sampling_without_replacement():
+    """The MXFP8 workload's routing (k = 8 distinct of E = 256 experts,
+    p_e proportional to (e+1)^-1.2, drawn by Gumbel-top-k) against an
+    independent sampler: numpy's sequential weighted draws without
+    replacement.  Checks distinct ids, the first draw's distribution
+    (categorical in p), every expert's inclusion rate and the mean number
+    of destination ranks per token at P = 8 (about 2.90 in identity order,
+    against 5.29 for uniform routing), which sets the workload's bytes."""
+    E, k, P, s = 256, 8, 8, 1.2
+    n_g, n_c = 60000, 20000
+    ids = W.draw_topk_ids(np.random.default_rng(123), n_g, E, k, "zipf", s)
+    assert all(len(set(r)) == k for r in ids[:2000])
+    assert ids.min() >= 0 and ids.max() < E
+    p = np.arange(1, E + 1, dtype=np.float64) ** -s
+    p /= p.sum()
+    rng = np.random.default_rng(7)
+    ref = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(n_c)])
+    # first draw (the ids come ordered by their key): categorical in p
+    f = np.bincount(ids[:, 0], minlength=E) / n_g
+    assert np.all(np.abs(f - p) <= 5 * np.sqrt(p * (1 - p) / n_g) + 1e-4)
+    # inclusion rates of every expert agree with the sequential sampler
+    inc_g = np.bincount(ids.ravel(), minlength=E) / n_g
+    inc_c = np.bincount(ref.ravel(), minlength=E) / n_c
+    se = np.sqrt(inc_g * (1 - inc_g) / n_g + inc_c * (1 - inc_c) / n_c)
+    assert np.all(np.abs(inc_g - inc_c) <= 5 * se + 1e-4)
+    # mean fan-out over P = 8 ranks of 32 contiguous experts
+    fan_g = np.array([len(np.unique(r // (E // P))) for r in ids])
+    fan_c = np.array([len(np.unique(r // (E // P))) for r in ref])
+    se_f = np.sqrt(fan_g.var() / n_g + fan_c.var() / n_c)
+    assert abs(fan_g.mean() - fan_c.mean()) <= 5 * se_f
+    assert fan_g.mean() == pytest.approx(2.90, abs=0.02)

@@ -1,7 +1,9 @@
 """Oracle vs a push-style pure-Python brute force on tiny random inputs,
 including duplicate ids, out-of-range / negative ids, ragged counts,
 P = 1 and k = 1.  Dispatch must agree exactly; combine sums must agree
-exactly (same order, both double)."""
+bit for bit: the fp32 sums with numpy float32 additions in the same
+(ascending rank) order, the exact sums with Python float sums, and the
+bf16 result with torch's round-to-nearest-even cast of the fp32 sum."""
 import numpy as np
 import pytest
 import torch
@@ -75,21 +77,48 @@ def test_dispatch_destination_subset_matches_full():
         assert np.array_equal(full[key][1:3], part[key])
 
 
+def _torch_bf16_bits(f32):
+    return torch.from_numpy(np.asarray(f32, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+
+
 @pytest.mark.parametrize("P,T,k,E", SHAPES)
 def test_combine_bf16_matches_bruteforce(P, T, k, E):
     rng = np.random.default_rng(77 + P * T)
     H = 8
     counts, payload, ids, weights, scales = _case(rng, P, T, k, E, H=H)
-    eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
-    ref, y = oracle.combine_bf16(counts, ids, eo, E=E)
+    # magnitudes spread over 2^-20 .. 2^20 so fp32 rounding shows in the sums
+    eo = _bf16_bits(rng.standard_normal((P, P * T, H)) * 2.0 ** rng.integers(-20, 21, (P, P * T, 1)))
+    got = oracle.combine_bf16(counts, ids, eo, E=E)
     want = bf.combine_bf16(counts, ids, eo, E)
+    want32 = bf.combine_bf16_fp32(counts, ids, eo, E)
     for s in range(P):
         for t in range(T):
             if t < counts[s]:
-                assert list(ref[s, t]) == want[(s, t)]
-                assert all(int(y[s, t, h]) == oracle.double_to_bf16(want[(s, t)][h]) for h in range(H))
+                assert list(got.exact[s, t]) == want[(s, t)]
+                assert np.array_equal(got.ref[s, t].view(np.uint32), want32[(s, t)].view(np.uint32))
+                assert np.array_equal(got.y[s, t], _torch_bf16_bits(want32[(s, t)]))
             else:
-                assert np.all(ref[s, t] == 0) and np.all(y[s, t] == 0)
+                assert np.all(got.ref[s, t] == 0) and np.all(got.exact[s, t] == 0) and np.all(got.y[s, t] == 0)
+
+
+def test_combine_fp32_sum_within_recursive_summation_bound():
+    """|fl32(sum) - sum| <= gamma_(m-1) * sum|terms| for m terms added one
+    by one (gamma_n = n u / (1 - n u), u = 2^-24): the fp32 reference is a
+    sum of exactly the token's terms, each rounded once per addition."""
+    rng = np.random.default_rng(78)
+    P, T, k, E, H = 8, 6, 8, 32, 64
+    counts, _, ids, _, _ = _case(rng, P, T, k, E, H=H, oob=False)
+    eo = _bf16_bits(rng.standard_normal((P, P * T, H)) * 2.0 ** rng.integers(-24, 25, (P, P * T, 1)))
+    got = oracle.combine_bf16(counts, ids, eo, E=E)
+    ev = torch.from_numpy(eo.view(np.int16)).view(torch.bfloat16).double().numpy()
+    u = 2.0 ** -24
+    for s in range(P):
+        for t in range(int(counts[s])):
+            dests = sorted({int(e) // (E // P) for e in ids[s, t]})
+            m = len(dests)
+            mag = np.abs(ev[dests, s * T + t]).sum(axis=0)
+            gamma = (m - 1) * u / (1 - (m - 1) * u)
+            assert np.all(np.abs(got.ref[s, t].astype(np.float64) - got.exact[s, t]) <= gamma * mag)
 
 
 def test_combine_token_agrees_with_array_form():
@@ -97,13 +126,61 @@ def test_combine_token_agrees_with_array_form():
     P, T, k, E, H = 4, 5, 3, 8, 16
     counts, _, ids, _, _ = _case(rng, P, T, k, E, H=H)
     eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
-    ref, y = oracle.combine_bf16(counts, ids, eo, E=E)
+    full = oracle.combine_bf16(counts, ids, eo, E=E)
     for s in range(P):
         for t in range(int(counts[s])):
-            r1, y1 = oracle.combine_token_bf16(ids[s, t], eo[:, s * T + t], E=E)
-            assert np.array_equal(r1, ref[s, t]) and np.array_equal(y1, y[s, t])
-    ref2, y2 = oracle.combine_bf16(counts, ids, eo, E=E, s0=2, s1=4)
-    assert np.array_equal(ref2, ref[2:4]) and np.array_equal(y2, y[2:4])
+            one = oracle.combine_token_bf16(ids[s, t], eo[:, s * T + t], E=E)
+            for a, b in zip(one, full):
+                assert np.array_equal(a, b[s, t])
+    part = oracle.combine_bf16(counts, ids, eo, E=E, s0=2, s1=4)
+    for a, b in zip(part, full):
+        assert np.array_equal(a, b[2:4])
+    # the sources' slots alone ([P, 2T, H] slice holding slots 2T .. 4T-1)
+    sl = oracle.combine_bf16(counts, ids, eo[:, 2 * T:4 * T], E=E, s0=2, s1=4, slot0=2 * T)
+    for a, b in zip(sl, full):
+        assert np.array_equal(a, b[2:4])
+    f8 = oracle.combine_fp8(counts, ids, eo, E=E, s0=1, s1=3)
+    f8s = oracle.combine_fp8(counts, ids, eo[:, T:3 * T], E=E, s0=1, s1=3, slot0=T)
+    for a, b in zip(f8, f8s):
+        assert np.array_equal(a, b)
+    with pytest.raises(AssertionError):
+        oracle.combine_bf16(counts, ids, eo[:, 2 * T:4 * T], E=E, s0=1, s1=4, slot0=2 * T)
+
+
+def test_fp8_combine_matches_bruteforce():
+    """The fp32 sum of the dequantised landing rows (torch's e4m3 decode
+    times 2^(scale - 127)), added in ascending rank order with numpy
+    float32, bit for bit; exact sums with Python floats."""
+    rng = np.random.default_rng(79)
+    P, T, k, E, H = 4, 5, 3, 8, 64
+    counts, _, ids, _, _ = _case(rng, P, T, k, E, H=H)
+    eo = _bf16_bits(rng.standard_normal((P, P * T, H)) * 2.0 ** rng.integers(-30, 31, (P, P * T, 1)))
+    got = oracle.combine_fp8(counts, ids, eo, E=E)
+    epr = E // P
+    for s in range(P):
+        for t in range(int(counts[s])):
+            dests = sorted({int(e) // epr for e in ids[s, t] if 0 <= int(e) < E})
+            acc = np.zeros(H, np.float32)
+            ex = [0.0] * H
+            for r in dests:
+                v = bf.fp8_dequantise(got.land_codes[s, r * T + t], got.land_scales[s, r * T + t])
+                acc = (acc + v.astype(np.float32)).astype(np.float32)
+                ex = [a + float(b) for a, b in zip(ex, v)]
+            assert np.array_equal(got.ref[s, t].view(np.uint32), acc.view(np.uint32))
+            assert list(got.exact[s, t]) == ex
+            assert np.array_equal(got.y[s, t], _torch_bf16_bits(acc))
+
+
+def test_reduce_scatterv_matches_bruteforce():
+    rng = np.random.default_rng(80)
+    P, H = 6, 24
+    sizes = np.array([2, 0, 5, 1, 3, 4], np.int32)
+    part = _bf16_bits(rng.standard_normal((P, int(sizes.sum()), H)) * 2.0 ** rng.integers(-20, 21, (P, int(sizes.sum()), 1)))
+    for r in range(P):
+        got = oracle.reduce_scatterv(sizes, part, r)
+        want = bf.reduce_scatterv_fp32(sizes, part, r)
+        assert np.array_equal(got.ref.view(np.uint32), want.view(np.uint32))
+        assert np.array_equal(got.out, _torch_bf16_bits(want))
 
 
 @pytest.mark.parametrize("P,T,k,E", SHAPES[:4])

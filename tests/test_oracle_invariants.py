@@ -65,10 +65,11 @@ def test_golden_combine(golden_dir):
         for q, row in enumerate(g["combine"]["eo"][r]):
             if row is not None:
                 eo[r, q] = row
-    ref, y = oracle.combine_bf16(g["counts"], np.array(g["ids"], np.int32), _bf16_bits(eo), E=g["E"])
+    ref, y, exact = oracle.combine_bf16(g["counts"], np.array(g["ids"], np.int32), _bf16_bits(eo), E=g["E"])
     for s, rows in enumerate(g["combine"]["expect_y"]):
         for t, want in enumerate(rows):
             assert ref[s, t].tolist() == want
+            assert exact[s, t].tolist() == want
             assert _bits_to_f(y[s, t]).tolist() == want
     # +0 for a token sent nowhere (rank 1 token 1)
     assert y[1, 1].tolist() == [0, 0]
@@ -83,9 +84,62 @@ def test_golden_agrs(golden_dir):
     assert oracle.allgatherv(sizes, rows).tolist() == g["expect_gather"]
     part = _bf16_bits(np.array(g["partial"], np.float32))
     for r in range(2):
-        ref, out = oracle.reduce_scatterv(sizes, part, r)
+        ref, out, exact = oracle.reduce_scatterv(sizes, part, r)
         assert ref.tolist() == g["expect_scatter"][r]
+        assert exact.tolist() == g["expect_scatter"][r]
         assert _bits_to_f(out).tolist() == g["expect_scatter"][r]
+
+
+def test_golden_fp32_order(golden_dir):
+    """fp32 sums in ascending rank order from +0, rounded once to bf16
+    (tests/golden/combine_fp32_order.json, worked by hand)."""
+    g = json.load(open(os.path.join(golden_dir, "combine_fp32_order.json")))
+    P, T, H = g["P"], g["T"], g["H"]
+    eo = np.full((P, P * T, H), np.nan, np.float32)
+    for r in range(P):
+        for q, row in enumerate(g["eo"][r]):
+            if row is not None:
+                eo[r, q] = row
+    eb = _bf16_bits(eo)
+    assert np.array_equal(_bits_to_f(eb)[~np.isnan(eo)], eo[~np.isnan(eo)])  # every term is a bf16 value
+    ref, y, exact = oracle.combine_bf16(g["counts"], np.array(g["ids"], np.int32), eb, E=g["E"])
+    for s in range(P):
+        if g["expect_ref"][s] is None:
+            assert not y[s].any()
+            continue
+        assert ref[s].tolist() == g["expect_ref"][s]
+        assert y[s].tolist() == g["expect_y_bits"][s]
+        assert _bits_to_f(y[s]).tolist() == g["expect_y"][s]
+        assert exact[s].tolist() == g["expect_exact"][s]
+    assert not np.signbit(ref[0, 0, 2])  # +0, not -0
+    rs = g["reduce_scatterv"]
+    part = _bf16_bits(np.array(rs["partial"], np.float32))
+    for r in range(P):
+        ref, out, exact = oracle.reduce_scatterv(np.array(rs["sizes"], np.int32), part, r)
+        assert ref.tolist() == rs["expect_ref"][r]
+        assert out.tolist() == rs["expect_out_bits"][r]
+        assert exact.tolist() == rs["expect_exact"][r]
+    f8 = g["fp8"]
+    H8 = f8["H"]
+    eo8 = np.zeros((P, P * T, H8), np.float32)
+    for col, terms in f8["terms"].items():
+        for r, v in enumerate(terms):
+            eo8[r, 0, int(col)] = v
+    eb8 = _bf16_bits(eo8)
+    codes, scales, ref, y, exact = oracle.combine_fp8(g["counts"], np.array(g["ids"], np.int32), eb8, E=g["E"],
+                                                      s0=0, s1=1)
+    for r in range(P):
+        land = r * T + 0  # rank r's row of source 0's token 0
+        assert scales[0, land].tolist() == f8["expect_scale_codes"][r]
+        assert [int(codes[0, land, 0]), int(codes[0, land, 32])] == f8["expect_codes_0_32"][r]
+        assert np.count_nonzero(codes[0, land]) == 2
+    for col in f8["terms"]:
+        h = int(col)
+        assert float(ref[0, 0, h]) == f8["expect_ref"][col]
+        assert float(exact[0, 0, h]) == f8["expect_exact"][col]
+        assert int(y[0, 0, h]) == f8["expect_y_bits"][col]
+    others = [h for h in range(H8) if str(h) not in f8["terms"]]
+    assert not ref[0, 0, others].any() and not y[0, 0, others].any()
 
 
 # ---------------------------------------------------------------- dispatch invariants
@@ -165,7 +219,7 @@ def test_identity_expert_combine(w):
             for r in np.unique(owners):
                 wsum = float(R.weights[s, t][owners == r].sum(dtype=np.float64))
                 eo[r, s * T + t] = (x[s, t] * wsum).astype(np.float32)
-    ref, y = oracle.combine_bf16(R.counts, R.ids, _bf16_bits(eo), E=w.E)
+    y = oracle.combine_bf16(R.counts, R.ids, _bf16_bits(eo), E=w.E).y
     yv = _bits_to_f(y)
     for s in range(P):
         n = int(R.counts[s])
@@ -181,14 +235,14 @@ def test_k1_and_p1_combine_single_term_is_exact():
     ids = rng.integers(0, E, (P, T, 1)).astype(np.int32)
     eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
     counts = np.array([6, 3, 0, 5], np.int32)
-    _, y = oracle.combine_bf16(counts, ids, eo, E=E)
+    y = oracle.combine_bf16(counts, ids, eo, E=E).y
     for s in range(P):
         for t in range(int(counts[s])):
             r = ids[s, t, 0] // (E // P)
             assert np.array_equal(y[s, t], eo[r, s * T + t])
     ids1 = rng.integers(0, E, (1, T, 3)).astype(np.int32)
     eo1 = _bf16_bits(rng.standard_normal((1, T, H)))
-    _, y1 = oracle.combine_bf16([T], ids1, eo1, E=E)
+    y1 = oracle.combine_bf16([T], ids1, eo1, E=E).y
     assert np.array_equal(y1[0], eo1[0])
 
 
@@ -199,8 +253,8 @@ def test_fp8_combine_error_bound_and_exact_values():
     counts = np.array([6, 6, 2, 5], np.int32)
     eo_f = rng.standard_normal((P, P * T, H)) * 2.0 ** rng.integers(-6, 6, (P, P * T, 1))
     eo = _bf16_bits(eo_f)
-    land_c, land_s, ref_q, y = oracle.combine_fp8(counts, ids, eo, E=E)
-    ref, _ = oracle.combine_bf16(counts, ids, eo, E=E)
+    land_c, land_s, _, _, ref_q = oracle.combine_fp8(counts, ids, eo, E=E)
+    ref = oracle.combine_bf16(counts, ids, eo, E=E).exact
     ev = _bits_to_f(eo)
     epr = E // P
     for s in range(P):
@@ -223,8 +277,8 @@ def test_fp8_combine_error_bound_and_exact_values():
     ints[..., 0] = 15.0 / 8.0  # fix the block maximum so the scale keeps 4 bits
     ints[..., 32] = 15.0 / 8.0
     eo2 = _bf16_bits(ints)
-    _, _, ref_q2, _ = oracle.combine_fp8(counts, ids, eo2, E=E)
-    ref2, _ = oracle.combine_bf16(counts, ids, eo2, E=E)
+    ref_q2 = oracle.combine_fp8(counts, ids, eo2, E=E).exact
+    ref2 = oracle.combine_bf16(counts, ids, eo2, E=E).exact
     assert np.array_equal(ref_q2, ref2)
 
 
@@ -248,15 +302,19 @@ def test_reduce_scatterv_matches_exact_sum():
     pv = _bits_to_f(part)
     off = np.concatenate([[0], np.cumsum(sizes)])
     for r in range(P):
-        ref, out = oracle.reduce_scatterv(sizes, part, r)
+        ref, out, exact = oracle.reduce_scatterv(sizes, part, r)
         assert ref.shape == (sizes[r], H)
+        u = 2.0 ** -24
         for i in range(sizes[r]):
             for h in range(H):
-                exact = math.fsum(pv[:, off[r] + i, h])
-                assert abs(ref[i, h] - exact) <= 1e-12 * np.abs(pv[:, off[r] + i, h]).sum()
+                fs = math.fsum(pv[:, off[r] + i, h])
+                mag = np.abs(pv[:, off[r] + i, h]).sum()
+                assert exact[i, h] == fs  # a handful of bf16 terms: the double sum is exact
+                # the fp32 sum: within the recursive summation bound of P terms
+                assert abs(float(ref[i, h]) - fs) <= (P - 1) * u / (1 - (P - 1) * u) * mag
     # P = 1: identity
     one = _bf16_bits(rng.standard_normal((1, 7, H)))
-    _, o1 = oracle.reduce_scatterv(np.array([7], np.int32), one, 0)
+    o1 = oracle.reduce_scatterv(np.array([7], np.int32), one, 0).out
     assert np.array_equal(o1, one[0])
 
 

@@ -57,16 +57,18 @@ def test_masked_combine_sums_live_ranks(alive):
     P, T, k, E, H = 4, 6, 3, 8, 8
     counts, _, ids, _, _ = _case(rng, P, T, k, E, H=H)
     eo = _bf16_bits(rng.standard_normal((P, P * T, H)))
-    ref, y = oracle.combine_bf16(counts, ids, eo, E=E, active=_mask(alive))
+    got = oracle.combine_bf16(counts, ids, eo, E=E, active=_mask(alive))
     want = bf.combine_bf16(counts, ids, eo, E, alive=alive)
+    want32 = bf.combine_bf16_fp32(counts, ids, eo, E, alive=alive)
     for s in range(P):
         for t in range(T):
             if (s, t) in want:
-                assert list(ref[s, t]) == want[(s, t)]
+                assert list(got.exact[s, t]) == want[(s, t)]
+                assert np.array_equal(got.ref[s, t].view(np.uint32), want32[(s, t)].view(np.uint32))
             else:
-                assert not ref[s, t].any() and not y[s, t].any()
+                assert not got.ref[s, t].any() and not got.y[s, t].any()
     # fp8 path: masked ranks contribute nothing either
-    _, _, rq, _ = oracle.combine_fp8(counts, ids, eo, E=E, active=_mask(alive))
+    rq = oracle.combine_fp8(counts, ids, eo, E=E, active=_mask(alive)).exact
     for s in range(P):
         if s not in alive:
             assert not rq[s].any()
