@@ -107,8 +107,10 @@ int check_params(const moe_ep_params *pp, Layout *lay)
         return fail(MOE_EP_ERR_INVALID_ARG, "DeepSeekFp8 payloads need hidden_size % 128 == 0");
     if (p.extra_payload_bytes_per_token < 0)
         return fail(MOE_EP_ERR_INVALID_ARG, "extra_payload_bytes_per_token may not be negative");
-    if (p.eplb_stats_num_experts < 0)
-        return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_num_experts must be non-negative");
+    // statistics of at most every expert (NVLinkTwoSidedAlltoAll class
+    // paragraph: EPLB statistics cover all num_experts experts)
+    if (p.eplb_stats_num_experts < 0 || p.eplb_stats_num_experts > p.num_experts)
+        return fail(MOE_EP_ERR_INVALID_ARG, "eplb_stats_num_experts must be in [0, num_experts]");
     if (p.hidden_size % 8 != 0)
         return fail(MOE_EP_ERR_INVALID_ARG, "combine rows need hidden_size % 8 == 0");
     if (p.combine_format == MOE_EP_COMBINE_FP8 && p.hidden_size % 32 != 0)

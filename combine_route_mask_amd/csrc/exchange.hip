@@ -230,7 +230,8 @@ __device__ void scan_destination(const DispatchArgs &a, int r)
         // EPLB statistics all-gather: row s of rank r's [P][n] matrix is
         // live rank s's statistics
         int32_t *dst = reinterpret_cast<int32_t *>(a.ws + (int64_t)r * a.region + a.off_eplb);
-        for (int i = threadIdx.x; i < a.P * a.n_eplb; i += kBlock)
+        const int64_t nst = (int64_t)a.P * a.n_eplb;
+        for (int64_t i = threadIdx.x; i < nst; i += kBlock)
             if ((a.active >> (i / a.n_eplb)) & 1u)
                 dst[i] = a.eplb[i];
     }

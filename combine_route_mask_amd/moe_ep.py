@@ -127,6 +127,17 @@ def _stream(stream) -> Optional[int]:
     return int(stream.cuda_stream)
 
 
+def _torch_stream(stream):
+    """The torch stream object of a stream argument (None: the current
+    stream; a raw hipStream_t handle is wrapped)."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream()
+    if isinstance(stream, int):
+        return torch.cuda.ExternalStream(stream)
+    return stream
+
+
 def _i32_array(vals: Sequence[int]):
     a = np.ascontiguousarray(np.asarray(vals, dtype=np.int32))
     return a, a.ctypes.data_as(C.POINTER(C.c_int32))
@@ -361,7 +372,10 @@ class MoeEpExchange:
         _need(expert_output.dtype == torch.bfloat16 and tuple(expert_output.shape) == (P, P * T, H),
               f"expert_output must be bf16 [P, P*T, H] = [{P}, {P * T}, {H}]")
         if output is None:
-            output = torch.zeros((P, T, H), dtype=torch.bfloat16, device=expert_output.device)
+            # zero-filled on the launch stream, so the fill is ordered before
+            # the combine's writes whatever the current stream is
+            with torch.cuda.stream(_torch_stream(stream)):
+                output = torch.zeros((P, T, H), dtype=torch.bfloat16, device=expert_output.device)
         _dev_contig(output, "output", self.workspace.device)
         _need(output.dtype == torch.bfloat16 and tuple(output.shape) == (P, T, H),
               "output must be bf16 [P, T, H]")

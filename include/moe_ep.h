@@ -103,7 +103,8 @@ typedef struct moe_ep_params {
     int32_t has_weights;         /* 1: top-k weights travel with tokens        */
     int32_t invalid_expert_id;   /* id written to empty slots (usually E)      */
     int32_t extra_payload_bytes_per_token; /* >= 0: room for extra bytes per token */
-    int32_t eplb_stats_num_experts; /* >= 0: n of the EPLB statistics all-gather */
+    int32_t eplb_stats_num_experts; /* n in [0, num_experts] of the EPLB statistics
+                                       all-gather (0: none)                        */
 } moe_ep_params;
 
 /* Where a dispatch's receive planes live.  Plane X of rank r starts at
@@ -138,17 +139,28 @@ typedef struct moe_ep_handle moe_ep_handle;
  * (NVLinkTwoSidedAlltoAll.is_platform_supported). */
 int moe_ep_is_supported(void);
 
-/* Bytes of one rank's workspace region for these parameters (every plane
- * 256-byte aligned).  0 when the parameters are invalid (see
- * moe_ep_last_error), including a region above 2^46 bytes or more than
- * 2^31 - 1 slots (ep_size * max_tokens_per_rank), which moe_ep_create
- * rejects with MOE_EP_ERR_CAPACITY.  Host-only, no device work. */
+/* size_per_rank of the [ep_size, size_per_rank] workspace
+ * (moe_a2a_dispatch, workspace parameter; NVLinkOneSidedConfig, first
+ * options paragraph: the dispatch workspace holds each token's activations
+ * in the dispatch format plus its routing, extra_payload_bytes_per_token
+ * more bytes per token and the EPLB statistics): bytes of one rank's
+ * region for these parameters, every plane 256-byte aligned.  0 when the
+ * parameters are invalid (see moe_ep_last_error), including a region above
+ * 2^46 bytes or more than 2^31 - 1 slots (ep_size * max_tokens_per_rank),
+ * which moe_ep_create rejects with MOE_EP_ERR_CAPACITY.  Host-only, no
+ * device work. */
 size_t moe_ep_workspace_bytes(const moe_ep_params *params);
 
-/* Create a handle over a caller-owned device workspace of P regions of
- * size_per_rank bytes each (region r at workspace + r * size_per_rank,
- * size_per_rank >= moe_ep_workspace_bytes and a multiple of 256, workspace
- * 256-byte aligned).  The workspace needs no initialisation. */
+/* Create a handle (NVLinkOneSidedConfig, first paragraph: a communication
+ * is made by create_communication with the exchange's parameters and
+ * backend options; vLLM FlashInferNVLinkTwoSidedManager: MoEEpCommParams)
+ * over a caller-owned device workspace of P regions of size_per_rank bytes
+ * each (region r at workspace + r * size_per_rank, size_per_rank >=
+ * moe_ep_workspace_bytes and a multiple of 256, workspace 256-byte
+ * aligned).  The workspace needs no initialisation; the handle keeps host
+ * state only.  Errors: MOE_EP_ERR_INVALID_ARG (bad parameters, NULL or
+ * misaligned workspace), MOE_EP_ERR_CAPACITY (region too small or too
+ * large), MOE_EP_ERR_UNSUPPORTED (no gfx950 device current). */
 int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_rank,
                   moe_ep_handle **out);
 

@@ -80,6 +80,8 @@ def test_workspace_bytes_layout(m):
     (dict(dispatch_format=7), -2), (dict(combine_format=5), -2),
     (dict(hidden_size=7200, dispatch_format="deepseek_fp8"), -1),  # H % 128
     (dict(extra_payload_bytes_per_token=-1), -1), (dict(eplb_stats_num_experts=-4), -1),
+    (dict(eplb_stats_num_experts=257), -1),      # statistics of more experts than exist
+    (dict(eplb_stats_num_experts=(1 << 31) - 1), -1),
     (dict(max_tokens_per_rank=1 << 30, ep_size=64), -4),
     (dict(max_tokens_per_rank=1 << 24, ep_size=64, hidden_size=1 << 20), -4),   # region above 2^46 B
 ])

@@ -4,9 +4,8 @@ every valid slot, invalid-id markers on every other slot, per-source
 counts, source offsets and the ascending valid-slot list.
 
 Sizes: the small cases span several 256-thread tiles and ragged tails;
-the full workloads run at their real shapes (the largest one compares
-every id plane and count in full and the payload planes of sampled
-destination ranks)."""
+the EP8 workloads run at their real shapes here, the EP64 ones in
+test_gpu_ep64.py."""
 import dataclasses
 
 import numpy as np
@@ -15,7 +14,7 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import DispatchCase, gpu_inputs, log, random_byte_case
+from tests.gpu_util import DispatchCase, bits16, check_bf16_sum, gpu_inputs, log, random_byte_case
 
 pytestmark = pytest.mark.gpu
 
@@ -202,15 +201,6 @@ def test_dispatch_full_ep8_mxfp8_zipf():
     _run(random_byte_case(W.EP8_MXFP8, W.EP8_MXFP8.seed))
 
 
-@pytest.mark.parametrize("w", [W.EP64_BF16, W.EP64_NVFP4], ids=lambda w: w.name)
-def test_dispatch_full_ep64(w):
-    c = random_byte_case(w, w.seed)
-    ex = _run(c, dests=[0, 37, 63])
-    ex.destroy()
-    del ex
-    torch.cuda.empty_cache()
-
-
 # Long rows (8 KB and more) are stored write-through when the launch's
 # payload writes are bounded by 256 MiB (N * min(P, k) * row) and
 # non-temporally above; the row loads go before the mask in steps of at
@@ -228,7 +218,7 @@ STORE_PATHS = [
 @pytest.mark.parametrize("w", STORE_PATHS, ids=lambda w: w.name)
 def test_dispatch_store_paths(w):
     c = random_byte_case(w, 41)
-    ex = _run(c, dests=None if w.P <= 8 else [0, 17, 63])
+    ex = _run(c)
     ex.destroy()
     del ex
     torch.cuda.empty_cache()
@@ -297,8 +287,8 @@ def test_two_handles_on_two_streams():
     for c, out in zip(cases, outs):
         _check(c, out)
     for w, c, eo, y in zip(ws, cases, eos, ys):
-        ref, _ = oracle.combine_bf16(c.counts, c.ids, eo.view(torch.int16).cpu().numpy().view(np.uint16), E=w.E)
-        yv = y.float().cpu().numpy().astype(np.float64)
+        o = oracle.combine_bf16(c.counts, c.ids, bits16(eo), E=w.E)
+        yb = bits16(y)
         for s in range(w.P):
             n = int(c.counts[s])
-            assert np.all(np.abs(yv[s, :n] - ref[s, :n]) <= 2.0 ** -7 * np.abs(ref[s, :n]) + 1e-3)
+            check_bf16_sum(yb[s, :n], o.ref[s, :n], o.y[s, :n], f"{w.name} source {s}")

@@ -1,10 +1,12 @@
 """GPU parity on seeded random configurations: every combination of the
 options the exchange takes, each case small, checked against the oracle
-to the same bars as the targeted tests (dispatch bit-exact; BF16 combine
-within 2^-7 |ref| + 1e-3 plus the fp32 accumulation term (m - 1) 2^-24
-sum|terms|, since row magnitudes here span 2^-20..2^20; FP8 landing planes
-bit-exact and the sum within bf16 rounding plus fp32 accumulation of the
-dequantised terms).
+to the same bars as the targeted tests: dispatch bit-exact; BF16 combine
+within 2^-7 |ref| + 1e-3 of the oracle's fp32 sum over ranks and equal to
+its bf16 result bit for bit (row magnitudes span 2^-20..2^20, so fp32
+rounding shows); FP8 landing planes and result bit-exact, and the result
+within 0.07 sum|terms| (plus half an e4m3 subnormal step per term) of the
+exact sum of the bf16 terms, the elements outside the literal bound being
+counted and logged.
 
 Drawn per case: P in 1..64, experts per rank 1..8 (E % 4 == 0), top_k up
 to 16 with duplicate and out-of-range ids, T and per-rank counts, the
@@ -22,7 +24,8 @@ import torch
 
 import oracle
 import workloads as W
-from tests.gpu_util import bf16_bits_to_f64, bits16, gpu_inputs, log, random_byte_case
+from tests.gpu_util import (bf16_bits_to_f64, bits16, check_bf16_sum, check_fp8_sum, fp8_terms_and_floor, gpu_inputs,
+                            log, random_byte_case)
 
 pytestmark = pytest.mark.gpu
 
@@ -75,7 +78,7 @@ def _cases(n=120, seed=20261202, wide=False):
         out.append(Case(w, has_weights=bool(rng.random() < 0.85),
                         invalid_id=int(rng.choice([E, -1, 12345])), alive=alive,
                         extra_bytes=int(rng.integers(1, 41)) if rng.random() < 0.3 else 0,
-                        n_eplb=int(rng.integers(1, 300)) if rng.random() < 0.3 else 0))
+                        n_eplb=min(E, int(rng.integers(1, 300))) if rng.random() < 0.3 else 0))
     return out
 
 
@@ -129,40 +132,28 @@ def _check_dispatch(cs, c, out, ex, want, extra, stats, active):
 
 def _check_combine_bf16(cs, c, y, eb, valid, active):
     w = cs.w
-    P, T = w.P, w.T
-    ref, _ = oracle.combine_bf16(c.counts, c.ids, eb, E=w.E, active=active)
+    o = oracle.combine_bf16(c.counts, c.ids, eb, E=w.E, active=active)
     yb = bits16(y)
-    ev = bf16_bits_to_f64(eb)
-    for s in range(P):
+    for s in range(w.P):
         rows = bf16_bits_to_f64(yb[s])
         if s not in cs.alive:
             assert np.all(rows == 7.0), f"rows of masked-off source {s} were written"
             continue
         n = int(c.counts[s])
-        # the rows' magnitudes differ by up to 2^40 between ranks, so beside
-        # the bf16 bar the fp32 accumulation of m terms may cost
-        # (m - 1) 2^-24 sum|terms|
-        mag = np.zeros((n, w.H))
-        nterms = np.zeros((n, 1))
-        for r in range(P):
-            vr = valid[r, s * T:s * T + n]
-            mag += np.where(vr[:, None], np.abs(ev[r, s * T:s * T + n]), 0.0)
-            nterms += vr[:, None]
-        acc = np.maximum(nterms - 1, 0) * 2.0 ** -24 * mag
-        err = np.abs(rows[:n] - ref[s, :n])
-        assert np.all(err <= 2.0 ** -7 * np.abs(ref[s, :n]) + 1e-3 + acc), \
-            f"source {s}: worst error {err.max()}"
+        check_bf16_sum(yb[s, :n], o.ref[s, :n], o.y[s, :n], f"source {s}")
         assert np.all(rows[n:] == 7.0), f"rows past the count of source {s} were written"
 
 
 def _check_combine_fp8(cs, c, ex, y, eb, valid, active):
     w = cs.w
     P, T, H = w.P, w.T, w.H
-    land_c, land_s, ref_q, _ = oracle.combine_fp8(c.counts, c.ids, eb, E=w.E, active=active)
+    o8 = oracle.combine_fp8(c.counts, c.ids, eb, E=w.E, active=active)
+    exact = oracle.combine_bf16(c.counts, c.ids, eb, E=w.E, active=active).exact
     gc, gs = ex.combine_landing()
     gc, gs = gc.cpu().numpy(), gs.cpu().numpy()
     yb = bits16(y)
     ev = bf16_bits_to_f64(eb)
+    viol, total = 0, 0
     for s in range(P):
         rows = bf16_bits_to_f64(yb[s])
         if s not in cs.alive:
@@ -172,22 +163,13 @@ def _check_combine_fp8(cs, c, ex, y, eb, valid, active):
         lv = np.zeros(P * T, bool)
         for r in range(P):
             lv[r * T:r * T + n] = valid[r, s * T:s * T + n]
-        assert np.array_equal(gc[s][lv], land_c[s][lv]), f"landing codes of source {s}"
-        assert np.array_equal(gs[s][lv], land_s[s][lv]), f"landing scales of source {s}"
-        mag = np.zeros((n, H))
-        floor = np.zeros((n, H))
-        nterms = np.zeros((n, 1))
-        for r in range(P):
-            vr = valid[r, s * T:s * T + n]
-            mag += np.where(vr[:, None], np.abs(ev[r, s * T:s * T + n]), 0.0)
-            nterms += vr[:, None]
-            e = land_s[s][r * T:r * T + n].astype(np.int64) - 127
-            floor += np.where(vr[:, None], np.repeat(2.0 ** (e - 10), 32, axis=1), 0.0)
-        acc = np.maximum(nterms - 1, 0) * 2.0 ** -24 * (1 + 2.0 ** -4) * (mag + floor)
-        rq = ref_q[s, :n]
-        assert np.all(np.abs(rows[:n] - rq) <= 2.0 ** -8 * np.abs(rq) + acc + 2.0 ** -126), \
-            f"source {s}: y vs the dequantised sum"
+        assert np.array_equal(gc[s][lv], o8.land_codes[s][lv]), f"landing codes of source {s}"
+        assert np.array_equal(gs[s][lv], o8.land_scales[s][lv]), f"landing scales of source {s}"
+        mag, floor = fp8_terms_and_floor(ev, valid, o8.land_scales[s], s, T, n, P)
+        viol += check_fp8_sum(yb[s, :n], o8.y[s, :n], exact[s, :n], mag, floor, f"source {s}")
+        total += n * H
         assert np.all(rows[n:] == 7.0), f"rows past the count of source {s} were written"
+    log(f"FP8 literal bound: {viol} of {total} elements outside 0.07 sum|terms|")
 
 
 @pytest.mark.parametrize("cs", CASES, ids=lambda cs: cs.name)
