@@ -19,6 +19,7 @@ struct moe_ep_handle {
     moe_ep_params p;
     uint8_t *ws;
     Layout lay;
+    uint8_t *scratch;                 // the static staging array on the handle's device
     bool dispatched;
     int32_t T;                        // step size of the last dispatch
     int32_t n[MOE_EP_MAX_RANKS];      // token counts of the last dispatch
@@ -219,6 +220,11 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
         return fail(MOE_EP_ERR_CAPACITY, "size_per_rank is below moe_ep_workspace_bytes(params)");
     if (!moe_ep_is_supported())
         return fail(MOE_EP_ERR_UNSUPPORTED, "no gfx950 (MI355X) device is current");
+    // the current device's staging array (once per device, kept)
+    void *scratch = nullptr;
+    hipError_t e = static_scratch(&scratch);
+    if (e != hipSuccess)
+        return fail(MOE_EP_ERR_HIP, std::string("static staging array lookup failed: ") + hipGetErrorString(e));
     moe_ep_handle *h = new (std::nothrow) moe_ep_handle;
     if (!h)
         return fail(MOE_EP_ERR_INVALID_ARG, "out of host memory");
@@ -227,6 +233,7 @@ int moe_ep_create(const moe_ep_params *params, void *workspace, size_t size_per_
     h->ws = static_cast<uint8_t *>(workspace);
     h->lay = L;
     h->lay.region = (int64_t)size_per_rank;
+    h->scratch = static_cast<uint8_t *>(scratch);
     {
         std::lock_guard<std::mutex> lk(g_handles_mu);
         g_handles.insert(h);
@@ -349,7 +356,14 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
     return ok();
 }
 
-int moe_ep_combine(moe_ep_handle *h, const void *expert_output, void *output, void *stream)
+} // extern "C"
+
+namespace {
+
+// Combine of the last dispatch.  static_land: the FP8 landing planes live
+// in the library's static staging array (codes [P][P*T][H], then scales
+// [P][P*T][H/32], one block per source rank) instead of the workspace.
+int run_combine(moe_ep_handle *h, const void *expert_output, void *output, void *stream, bool static_land)
 {
     if (!live_handle(h))
         return fail(MOE_EP_ERR_INVALID_ARG, "invalid or destroyed handle");
@@ -360,6 +374,7 @@ int moe_ep_combine(moe_ep_handle *h, const void *expert_output, void *output, vo
     if (!output || !aligned(output, 16))
         return fail(MOE_EP_ERR_INVALID_ARG, "output must be a 16-byte aligned device pointer");
     const moe_ep_params &p = h->p;
+    const bool fp8 = p.combine_format == MOE_EP_COMBINE_FP8;
     CombineArgs a;
     std::memset(&a, 0, sizeof a);
     a.eo = static_cast<const uint16_t *>(expert_output);
@@ -367,19 +382,47 @@ int moe_ep_combine(moe_ep_handle *h, const void *expert_output, void *output, vo
     a.ws = h->ws;
     a.region = h->lay.region;
     a.off_masks = h->lay.masks;
+    a.land = h->ws;
+    a.land_stride = h->lay.region;
     a.off_land_codes = h->lay.land_codes;
     a.off_land_scales = h->lay.land_scales;
     a.P = p.ep_size;
     a.T = h->T;
     a.H = p.hidden_size;
+    if (static_land && fp8) {
+        const int64_t slots = (int64_t)a.P * a.T;
+        const int64_t codes = slots * a.H, scales = slots * (a.H / 32);
+        const int64_t stride = align256(codes + scales);
+        if (stride > kStaticScratchBytes / a.P)
+            return fail(MOE_EP_ERR_CAPACITY,
+                        "FP8 landing planes of this step need " + std::to_string(stride * a.P) +
+                            " bytes; the static staging array holds " + std::to_string(kStaticScratchBytes));
+        a.land = h->scratch;
+        a.land_stride = stride;
+        a.off_land_codes = 0;
+        a.off_land_scales = codes;
+    }
     for (int s = 0; s < p.ep_size; ++s)
         a.n[s] = h->n[s];
-    hipError_t e = p.combine_format == MOE_EP_COMBINE_FP8
-                       ? launch_combine_fp8(a, static_cast<hipStream_t>(stream))
+    hipError_t e = fp8 ? launch_combine_fp8(a, static_cast<hipStream_t>(stream))
                        : launch_combine_bf16(a, static_cast<hipStream_t>(stream));
     if (e != hipSuccess)
         return fail(MOE_EP_ERR_HIP, std::string("combine launch failed: ") + hipGetErrorString(e));
     return ok();
+}
+
+} // namespace
+
+extern "C" {
+
+int moe_ep_combine(moe_ep_handle *h, const void *expert_output, void *output, void *stream)
+{
+    return run_combine(h, expert_output, output, stream, false);
+}
+
+int moe_ep_combine_noalloc(moe_ep_handle *h, const void *expert_output, void *output, void *stream)
+{
+    return run_combine(h, expert_output, output, stream, true);
 }
 
 int moe_ep_destroy(moe_ep_handle *h)

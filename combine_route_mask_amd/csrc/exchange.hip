@@ -14,6 +14,7 @@
 // (global_load/store_dwordx4); a workgroup reads a token row once and
 // writes it to every destination in its mask.
 #include <algorithm>
+#include <mutex>
 
 #include "formats.h"
 #include "memory_ops.h"
@@ -686,8 +687,9 @@ __device__ __forceinline__ void fp8_quant_item(const CombineArgs &a, int64_t w, 
         e[h] = c * (BS * 16) + h * (BS * 8) + threadIdx.x * 8;
         act[h] = e[h] < a.H;
     }
-    uint8_t *land = a.ws + (int64_t)s * a.region;
-    const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
+    const uint64_t mask = *reinterpret_cast<const uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks +
+                                                              (int64_t)t * 8);
+    uint8_t *land = a.land + (int64_t)s * a.land_stride;
     const uint8_t *src = reinterpret_cast<const uint8_t *>(a.eo) + q * a.H * 2;
     uint64_t m = mask;
     while (m) {
@@ -762,8 +764,9 @@ __device__ __forceinline__ void fp8_gather_item(const CombineArgs &a, int64_t w,
     }
     if (t >= a.n[s] || !act[0])
         return;
-    const uint8_t *land = a.ws + (int64_t)s * a.region;
-    const uint64_t mask = *reinterpret_cast<const uint64_t *>(land + a.off_masks + (int64_t)t * 8);
+    const uint64_t mask = *reinterpret_cast<const uint64_t *>(a.ws + (int64_t)s * a.region + a.off_masks +
+                                                              (int64_t)t * 8);
+    const uint8_t *land = a.land + (int64_t)s * a.land_stride;
     float acc[2][8];
 #pragma unroll
     for (int h = 0; h < 2; ++h)
@@ -996,6 +999,40 @@ hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s)
     if (units % 64 == 0)
         return launch_combine_fp8_bs<64>(a, s);
     return launch_combine_fp8_bs<256>(a, s);
+}
+
+// The library's staging array for callers that cannot allocate: the FP8
+// combine landing planes of moe_ep_combine_noalloc.  File scope, so every
+// GPU the library runs on holds one copy from module load until the process
+// ends.  In host code its name is a host-side stand-in, not a device
+// address: kernels get the address static_scratch() looked up.
+static __device__ __align__(256) uint8_t scratch[kStaticScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices]; // per device, looked up once with that device current
+} // namespace
+
+hipError_t static_scratch(void **ptr)
+{
+    *ptr = nullptr;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= kMaxDevices)
+        return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess)
+            return e;
+        g_scratch_ptr[dev] = p;
+    }
+    *ptr = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 } // namespace moe_ep

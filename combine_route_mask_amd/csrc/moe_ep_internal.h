@@ -43,8 +43,10 @@ struct DispatchArgs {
 struct CombineArgs {
     const uint16_t *eo;              // [P][P*T][H] bf16
     uint16_t *out;                   // [P][T][H] bf16
-    uint8_t *ws;
-    int64_t region, off_masks, off_land_codes, off_land_scales;
+    uint8_t *ws;                     // token masks of source s at ws + s * region + off_masks
+    int64_t region, off_masks;
+    uint8_t *land;                   // FP8 landing planes of source s at land + s * land_stride
+    int64_t land_stride, off_land_codes, off_land_scales;
     int32_t P, T, H;
     int32_t n[MOE_EP_MAX_RANKS];
 };
@@ -76,6 +78,13 @@ hipError_t launch_dispatch(const DispatchArgs &a, hipStream_t s);
 hipError_t launch_combine_bf16(const CombineArgs &a, hipStream_t s);
 hipError_t launch_combine_fp8(const CombineArgs &a, hipStream_t s);
 hipError_t launch_allgatherv(const AllGatherArgs &a, int64_t rows, hipStream_t s);
+
+// Bytes of the library's static staging array (one per GPU): the FP8
+// combine landing planes of the combine entry point that allocates nothing.
+constexpr int64_t kStaticScratchBytes = MOE_EP_STATIC_SCRATCH_BYTES;
+// Device address of the current device's staging array (looked up once per
+// device and kept); hipSuccess or the lookup's error.
+hipError_t static_scratch(void **ptr);
 hipError_t launch_reduce_scatterv(const ReduceScatterArgs &a, int64_t rows, hipStream_t s);
 
 } // namespace moe_ep

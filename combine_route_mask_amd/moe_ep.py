@@ -37,8 +37,9 @@ _COMBINE_NAMES = {"bf16": COMBINE_BF16, "fp8": COMBINE_FP8}
 
 # Every symbol include/moe_ep.h declares.
 EXPORTS = ("moe_ep_is_supported", "moe_ep_workspace_bytes", "moe_ep_create", "moe_ep_dispatch",
-           "moe_ep_combine", "moe_ep_destroy", "moe_ep_allgatherv", "moe_ep_reduce_scatterv",
-           "moe_ep_last_error")
+           "moe_ep_combine", "moe_ep_combine_noalloc", "moe_ep_destroy", "moe_ep_allgatherv",
+           "moe_ep_reduce_scatterv", "moe_ep_last_error")
+STATIC_SCRATCH_BYTES = 64 << 20  # MOE_EP_STATIC_SCRATCH_BYTES
 
 
 class MoeEpError(RuntimeError):
@@ -93,6 +94,8 @@ def _load(path: str = LIB_PATH):
     L.moe_ep_dispatch.restype = C.c_int
     L.moe_ep_combine.argtypes = [vp, vp, vp, vp]
     L.moe_ep_combine.restype = C.c_int
+    L.moe_ep_combine_noalloc.argtypes = [vp, vp, vp, vp]
+    L.moe_ep_combine_noalloc.restype = C.c_int
     L.moe_ep_destroy.argtypes = [vp]
     L.moe_ep_destroy.restype = C.c_int
     L.moe_ep_allgatherv.argtypes = [i32, C.POINTER(i32), i32, C.POINTER(Plane), vp]
@@ -194,6 +197,12 @@ def moe_ep_dispatch(handle, hidden, scales, topk_ids, topk_weights, num_tokens,
 
 def moe_ep_combine(handle, expert_output, output, stream=None) -> None:
     _check(lib.moe_ep_combine(handle, _ptr(expert_output), _ptr(output), _stream(stream)))
+
+
+def moe_ep_combine_noalloc(handle, expert_output, output, stream=None) -> None:
+    """moe_ep_combine staging the FP8 landing planes in the library's static
+    array (no allocation anywhere; output must be given)."""
+    _check(lib.moe_ep_combine_noalloc(handle, _ptr(expert_output), _ptr(output), _stream(stream)))
 
 
 def moe_ep_destroy(handle) -> None:

@@ -217,6 +217,29 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
  */
 int moe_ep_combine(moe_ep_handle *h, const void *expert_output, void *output, void *stream);
 
+/*
+ * moe_ep_combine for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid it): the
+ * same combine of the last dispatch, with the same arguments and result,
+ * but an FP8 combine stages its landing planes (e4m3 codes [P][P*T][H],
+ * then e8m0 scales [P][P*T][H/32], per source rank) in the library's own
+ * static device array of MOE_EP_STATIC_SCRATCH_BYTES instead of the
+ * workspace; a BF16 combine stages nothing and runs as moe_ep_combine.
+ * Allocates nothing (no hipMalloc, no allocating library call).
+ *  - MOE_EP_ERR_CAPACITY when the step's landing planes,
+ *    P * round_up_256(P*T*(H + H/32)) bytes for the last dispatch's T,
+ *    exceed the array (e.g. P = 8, H = 7168 fits up to T = 128);
+ *  - each GPU holds one array from library load until the process ends,
+ *    shared by every call on that GPU; it keeps the last call's contents
+ *    and needs no clearing (every landing row a call reads, it writes
+ *    first), so calls on one GPU that overlap in time (other streams, other
+ *    threads) race on it;
+ *  - the workspace's landing-plane views (combine_payload_offset) are not
+ *    written by this call.
+ */
+#define MOE_EP_STATIC_SCRATCH_BYTES (64ll << 20)
+int moe_ep_combine_noalloc(moe_ep_handle *h, const void *expert_output, void *output, void *stream);
+
 /* Release the handle.  Idempotent and NULL-safe; frees no caller memory. */
 int moe_ep_destroy(moe_ep_handle *h);
 
