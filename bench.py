@@ -121,9 +121,10 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
             "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
             "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
             "launches": len(vs), "source_digest": source_digest()}))
-    cfg = "" if config == "ep8" else f" --config {config}"
-    if config == "agrs":  # the AgRs step runs as an extra workload of the default bench
-        run = "python3 <repo>/bench.py --also agrs --no-cpu-baseline --no-graph --steps 3 --warmup 2"
+    cfg = f" --config {config}"
+    if config == "agrs":  # the AgRs step runs as an extra workload of another one
+        run = ("python3 <repo>/bench.py --config ep8 --cache warm --also agrs --no-cpu-baseline --no-graph "
+               "--steps 3 --warmup 2")
     else:
         run = (f"python3 <repo>/bench.py{cfg} --also '' --no-cpu-baseline --no-graph "
                f"--steps {6 if config == 'ep8' else 3} --warmup 2")
