@@ -55,12 +55,17 @@
 // for outputs below MOE_EP_COMBINE_LARGE_BYTES and for larger ones.  Output
 // rows are not read again within a step, so they never stay in the caches:
 // written through for outputs of at most MOE_EP_WT_BYTES, non-temporal
-// above.
+// above.  Large outputs: one vector per thread of 128-thread workgroups (a
+// 7168-wide row in seven 2 KB pieces) and four ranks in flight, one item per
+// workgroup; on the EP64 workload (same buffers) 713 us against 749 us for
+// four vectors per thread in 256-thread workgroups: each workgroup's output
+// store is one 2 KB piece, so the combine's writes reach HBM as a denser
+// front among its reads (64 / 448 / 896 threads: 756 / 744 / 729 us).
 #ifndef MOE_EP_COMBINE_SMALL
 #define MOE_EP_COMBINE_SMALL 1, 8
 #endif
 #ifndef MOE_EP_COMBINE_LARGE
-#define MOE_EP_COMBINE_LARGE 4, 2
+#define MOE_EP_COMBINE_LARGE 1, 4
 #endif
 // Threads per workgroup of the small-output shape: at H = 7168 a row is
 // 896 16-byte vectors, seven chunks of 128 with no idle lanes (256-thread
@@ -70,7 +75,13 @@
 #define MOE_EP_COMBINE_SMALL_BLOCK 128
 #endif
 #ifndef MOE_EP_COMBINE_LARGE_BLOCK
-#define MOE_EP_COMBINE_LARGE_BLOCK 256 // threads per workgroup of the large-output shape
+#define MOE_EP_COMBINE_LARGE_BLOCK 128 // threads per workgroup of the large-output shape
+#endif
+// Most workgroups of a BF16 combine launch: up to this many items each
+// workgroup runs one item (its token's route mask in one scalar load), above
+// it they loop.  The EP64 combine has 229376 items.
+#ifndef MOE_EP_COMBINE_GRID_CAP
+#define MOE_EP_COMBINE_GRID_CAP (1ll << 22)
 #endif
 #ifndef MOE_EP_FP8_GATHER
 #define MOE_EP_FP8_GATHER 2 // ranks per round in the FP8 combine kernels
@@ -941,7 +952,7 @@ static hipError_t launch_combine_shape(const CombineArgs &a, hipStream_t s)
 {
     const int64_t nchunk = ceil_div((int64_t)a.H >> 3, BS * VPT);
     const int64_t items = (int64_t)a.P * a.T * nchunk;
-    const dim3 grid((unsigned)grid_for(items));
+    const dim3 grid((unsigned)std::max<int64_t>(1, std::min<int64_t>(items, MOE_EP_COMBINE_GRID_CAP)));
     if ((int64_t)grid.x == items)
         hipLaunchKernelGGL((combine_bf16_kernel<BS, VPT, G, WT, true>), grid, dim3(BS), 0, s, a, nchunk);
     else
