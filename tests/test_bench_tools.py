@@ -93,3 +93,27 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     assert r["hbm_bytes_per_launch"] == int(round((1100.0 * 2 + 300.0) * 1024))
     assert r["source_digest"] == bench.source_digest()
     assert open(out).read().count("\n{") == 1
+
+
+def test_also_plan_cache_states():
+    """--also entries are warm unless suffixed '-cold'; the headline in its own
+    cache state is not repeated; warm and cold runs of one workload share one
+    entry (one set of buffers)."""
+    import argparse
+    a = argparse.Namespace(config="ep64", cache="cold", also="ep64,ep64-cold,ep8,ep8-cold,agrs,ep8")
+    assert bench.also_plan(a) == {"ep64": [False], "ep8": [False, True], "agrs": [False]}
+    a = argparse.Namespace(config="ep8", cache="warm", also="ep8,ep8-cold,ep64-cold")
+    assert bench.also_plan(a) == {"ep8": [True], "ep64": [True]}
+    assert bench.also_plan(argparse.Namespace(config="ep64", cache="cold", also="")) == {}
+
+
+def test_step_bytes_of_the_headline_workload():
+    """The EP64 headline's algorithmic bytes (the dispatch formula with N
+    tokens, M pairs, 14336-byte rows, k = 8): the roofline's bytes per launch."""
+    import workloads as W
+    w = W.EP64_BF16
+    N, M = 32768, 251630
+    b = bench.step_bytes(w, N, M)
+    row, k, P, T = 14336, 8, 64, 512
+    assert b["dispatch"] == N * k * 8 + N * row + M * (row + 8 * k) + (P * P * T - M) * 4 * k == 4154387904
+    assert b["combine"] == M * 2 * 7168 + N * 2 * 7168
