@@ -87,3 +87,41 @@ def test_noalloc_combine_rejects_steps_beyond_the_array():
         n = int(c.counts[s])
         assert np.array_equal(yb[s, :n], o.y[s, :n])
     ex.destroy()
+
+
+def test_noalloc_combine_replays_from_a_captured_graph():
+    """Captured into a HIP graph (a caller that cannot allocate inside the
+    capture), replayed three times with eager work between the replays that
+    rewrites the shared static array (a combine of another step through the
+    same entry point): every replay equals the eager call bit for bit."""
+    from combine_route_mask_amd import moe_ep
+    from combine_route_mask_amd.moe_ep import MoeEpExchange
+    w = dataclasses.replace(BASE, T=64, n_lo=20, n_hi=64)
+    ex = MoeEpExchange(w.P, w.E, w.k, w.T, w.H, combine_format="fp8")
+    c, eo = _step(ex, w, 94)
+    other = MoeEpExchange(w.P, w.E, w.k, w.T, w.H, combine_format="fp8")
+    c2, eo2 = _step(other, w, 95)
+    y_ref = torch.zeros((w.P, w.T, w.H), dtype=torch.bfloat16, device="cuda")
+    moe_ep.moe_ep_combine_noalloc(ex.handle, eo, y_ref)
+    y = torch.zeros_like(y_ref)
+    y2 = torch.zeros_like(y_ref)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe_ep.moe_ep_combine_noalloc(ex.handle, eo, y)
+    torch.cuda.synchronize()
+    for i in range(3):
+        y.fill_(0)
+        moe_ep.moe_ep_combine_noalloc(other.handle, eo2, y2)  # overwrites the static array
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16)), f"replay {i} differs from the eager call"
+    o = oracle.combine_fp8(c.counts, c.ids, bits16(eo), E=w.E)
+    yb = bits16(y)
+    for s in range(w.P):
+        n = int(c.counts[s])
+        assert np.array_equal(yb[s, :n], o.y[s, :n])
+    del g
+    ex.destroy()
+    other.destroy()
