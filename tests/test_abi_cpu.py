@@ -111,9 +111,11 @@ def test_calls_on_bad_handles(m):
     assert m.lib.moe_ep_dispatch(None, C.c_void_p(256), None, None, None, C.c_void_p(256), None,
                                  counts, 0, None, None, None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_combine(None, C.c_void_p(256), C.c_void_p(256), None) == m.ERR_INVALID_ARG
+    assert m.lib.moe_ep_combine_noalloc(None, C.c_void_p(256), C.c_void_p(256), None) == m.ERR_INVALID_ARG
     bogus = C.c_void_p(0x1234560)
     assert m.lib.moe_ep_dispatch(bogus, C.c_void_p(256), None, None, None, C.c_void_p(256), None,
                                  counts, 0, None, None, None) == m.ERR_INVALID_ARG
+    assert m.lib.moe_ep_combine_noalloc(bogus, C.c_void_p(256), C.c_void_p(256), None) == m.ERR_INVALID_ARG
     assert m.lib.moe_ep_destroy(None) == 0
     assert m.lib.moe_ep_destroy(bogus) == 0  # unknown handles are ignored
 
