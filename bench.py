@@ -21,6 +21,11 @@ line:
                committed rocprofv3 counter summary, null when the kernel
                sources have changed since it was taken
   cpu_baseline the CPU oracle on a bounded sample of the same workload
+  reference_kernels
+               plain kernels moving the headline step's payload bytes in its
+               patterns on its own buffers (scatter, gather-sum, the gather
+               without stores, whole-buffer fill and read), timed like the
+               step's launches: what its routing work costs over them
   also         the other workloads (--also), warm, or cold with a '-cold'
                suffix
 
@@ -441,6 +446,114 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
             "combine_ms": comb_ms, "wall_s": wall}
 
 
+CEILINGS_LIB = os.path.join(ROOT, "combine_route_mask_amd", "libmoe_ep_ceilings.so")
+
+
+def destination_masks(w, R) -> np.ndarray:
+    """[P*T] uint64, entry s*T + t: bit r set when token t of rank s has an
+    expert on rank r (contiguous ownership, E/P experts per rank; ids outside
+    [0, E) route nowhere); 0 for rows t >= n_s.  Popcounts sum to M."""
+    assert w.P <= 64
+    epr = w.E // w.P
+    ids = R.ids.astype(np.int64)
+    valid = (ids >= 0) & (ids < w.E)
+    owner = np.where(valid, ids, 0) // epr
+    bits = np.where(valid, np.left_shift(np.uint64(1), owner.astype(np.uint64)), np.uint64(0))
+    m = np.bitwise_or.reduce(bits, axis=2)
+    m[np.arange(w.T)[None, :] >= np.asarray(R.counts)[:, None]] = 0
+    return m.reshape(-1)
+
+
+def load_ceilings(path: str = CEILINGS_LIB):
+    import ctypes as C
+    lib = C.CDLL(path)
+    vp, i64, i32 = C.c_void_p, C.c_int64, C.c_int32
+    lib.ceil_scatter.argtypes = [vp, i64, i64, vp, i64, i32, vp, i64, i64, vp]
+    lib.ceil_gather.argtypes = [vp, i64, i32, vp, i64, i64, vp, i64, i32, vp]
+    lib.ceil_fill.argtypes = [vp, i64, vp]
+    lib.ceil_read.argtypes = [vp, i64, vp, i64, vp]
+    for f in (lib.ceil_scatter, lib.ceil_gather, lib.ceil_fill, lib.ceil_read):
+        f.restype = C.c_int
+    return lib
+
+
+def reference_kernels(setup, m, reps=5, flush_bytes=0):
+    """Plain reference kernels (libmoe_ep_ceilings.so) on the step's own
+    buffers, each launch timed alone with HIP events on the launch stream
+    (after the cache flush when flush_bytes): the dispatch's payload scatter
+    into the workspace's receive planes, the BF16 combine's gather-sum from
+    the expert outputs into the output (and the same with no output stores),
+    a fill of the whole workspace and a read of the whole expert-output
+    buffer.  They move the exchange's bytes in its patterns with none of its
+    routing work, so exchange / reference time is what that work costs on
+    these allocations.  BF16 dispatch and combine only; run after the step's
+    own checks (the gather leaves truncated sums in the output)."""
+    import ctypes as C
+    import torch
+    w = setup.w
+    if w.fmt != "bf16" or w.combine != "bf16" or w.P > 64:
+        return None
+    try:
+        lib = load_ceilings()
+    except OSError as e:
+        return {"error": f"reference kernels not built: {e}"}
+    st = torch.cuda.current_stream()
+    sp = C.c_void_p(st.cuda_stream)
+    masks = torch.from_numpy(destination_masks(w, setup.R).view(np.int64)).cuda()
+    row = 2 * w.H
+    ntok = w.P * w.T
+    ex = setup.ex
+    ws, spr = ex.workspace, ex.size_per_rank
+    pay = setup.views["payload"]
+    pay_off = pay.data_ptr() - ws.data_ptr()
+    sink = torch.empty(256 * 8 * 8, dtype=torch.int32, device="cuda")
+    N, M = setup.N, setup.M
+    eo_bytes = setup.eo.numel() * 2
+    runs = {
+        "scatter": (lambda: lib.ceil_scatter(setup.payload.data_ptr(), setup.payload.numel() * 2, row,
+                                             masks.data_ptr(), ntok, w.P, pay.data_ptr(), spr,
+                                             ws.numel() - pay_off, sp), (N + M) * row),
+        "gather": (lambda: lib.ceil_gather(setup.eo.data_ptr(), ntok * row, w.P, masks.data_ptr(), ntok,
+                                           row, setup.out.data_ptr(), setup.out.numel() * 2, 1, sp),
+                   (M + N) * row),
+        "gather_reads_only": (lambda: lib.ceil_gather(setup.eo.data_ptr(), ntok * row, w.P, masks.data_ptr(),
+                                                      ntok, row, setup.out.data_ptr(), setup.out.numel() * 2,
+                                                      0, sp), M * row),
+        "fill_workspace": (lambda: lib.ceil_fill(ws.data_ptr(), ws.numel(), sp), ws.numel()),
+        "read_expert_output": (lambda: lib.ceil_read(setup.eo.data_ptr(), eo_bytes, sink.data_ptr(),
+                                                     sink.numel(), sp), eo_bytes),
+    }
+    assert setup.eo.shape == (w.P, ntok, w.H) and setup.out.shape == (w.P, w.T, w.H)
+    assert setup.payload.is_contiguous() and setup.eo.is_contiguous() and setup.out.is_contiguous()
+    assert pay.stride(0) == spr and pay.stride(1) == row and pay_off + ntok * row <= spr
+    flush = _Flush(flush_bytes) if flush_bytes else None
+    res = {}
+    for name, (fn, nbytes) in runs.items():
+        if fn():  # untimed first launch (checks the arguments)
+            raise RuntimeError(f"reference kernel {name}: bad arguments")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, b in ev:
+            if flush is not None:
+                flush()
+            a.record(st)
+            fn()
+            b.record(st)
+        torch.cuda.synchronize()
+        ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+        res[name] = {"us": ms * 1e3, "bytes": int(nbytes), "GBps": nbytes / (ms / 1e3) / 1e9}
+    del flush
+    res["dispatch_over_scatter"] = m["dispatch_ms"] * 1e3 / res["scatter"]["us"]
+    res["combine_over_gather"] = m["combine_ms"] * 1e3 / res["gather"]["us"]
+    res["what"] = ("plain kernels on the step's own buffers, each launch timed alone"
+                   + (" after the cache flush" if flush_bytes else "") +
+                   ": scatter = payload rows read once and stored at their slot of every destination "
+                   "rank's receive plane (N + M rows), gather = per-token sum of its M rows of "
+                   "expert output plus the N output rows, gather_reads_only = the same with the sum "
+                   "kept only on a pattern match (no output stores)")
+    return res
+
+
 def trace_summary(trace_csv: str, workloads: list) -> str:
     """Markdown table of per-launch exchange-kernel durations from a
     rocprofv3 kernel-trace CSV of a bench run, grouped by workload (a new
@@ -451,8 +564,10 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
     all-gatherv; combine side: the combine kernels, reduce-scatterv) ran
     since this instance's previous launch, as in the step graphs; "alone":
     none did, as in the per-kernel graphs whose launch times the bench
-    reports.  The first launch of an instance in a workload is left out
-    (warm-up)."""
+    reports.  The plain reference kernels (scatter_kernel, gather_kernel,
+    fill_kernel, read_kernel) get context "reference" and leave the others'
+    contexts alone.  The first launch of an instance in a workload is left
+    out (warm-up)."""
     import collections
     import csv
     import re
@@ -460,6 +575,7 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
     ours = ("dispatch_kernel", "combine_bf16_kernel", "combine_fp8_quant_kernel",
             "combine_fp8_gather_kernel", "allgatherv_kernel", "reduce_scatterv_kernel")
     dispatch_side = ("dispatch_kernel", "allgatherv_kernel")
+    reference = ("scatter_kernel", "gather_kernel", "fill_kernel", "read_kernel")
     rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
     phase, ran, after_flush, seen = 0, False, False, set()
     sides_since = collections.defaultdict(set)  # instance -> sides launched since its last launch
@@ -473,10 +589,18 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
             after_flush = True
             continue
         m = re.search(r"(\w+_kernel(<[^(]*>)?)\(", name)
-        if not m or m.group(1).split("<")[0] not in ours:
+        if not m or m.group(1).split("<")[0] not in ours + reference:
+            continue
+        inst, cold, after_flush = m.group(1), after_flush, False
+        if inst.split("<")[0] in reference:
+            if (phase, inst) not in seen:
+                seen.add((phase, inst))
+                continue
+            wg = int(r["Grid_Size_X"]) // int(r["Workgroup_Size_X"])
+            dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+            groups[(phase, inst, wg, "cold" if cold else "warm", "reference")].append(dur)
             continue
         ran = True
-        inst, cold, after_flush = m.group(1), after_flush, False
         side = "dispatch" if inst.startswith(dispatch_side) else "combine"
         ctx = "step" if (sides_since[inst] - {side}) else "alone"
         sides_since[inst] = set()
@@ -635,6 +759,8 @@ def main():
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-reference-kernels", action="store_true",
+                    help="skip the plain reference kernels on the headline buffers")
     ap.add_argument("--cpu-budget", type=float, default=12.0)
     ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
                     help="print the per-workload kernel-duration table of a rocprofv3 kernel trace "
@@ -678,6 +804,10 @@ def main():
     m = measure(setup, args.steps, args.warmup, flush_bytes=(1 << 30) if cold else 0,
                 graphs=not args.no_graph)
     res, b = summarize(setup, m)
+    ref_kernels = None
+    if not args.no_reference_kernels:
+        print(f"[bench] reference kernels on the {w.name} buffers", file=sys.stderr, flush=True)
+        ref_kernels = reference_kernels(setup, m, flush_bytes=(1 << 30) if cold else 0)
     setup.free()
     torch.cuda.empty_cache()
     print(f"[bench] {w.name} ({args.cache}): {res['ms_per_step']*1e3:.1f} us/step", file=sys.stderr, flush=True)
@@ -741,6 +871,7 @@ def main():
         "detail": res,
         "roofline": roofline,
         "cpu_baseline": cpu,
+        "reference_kernels": ref_kernels,
         "device_copy_context": {"torch_copy_GBps": calib["copy_GBps"], "torch_fill_GBps": calib["fill_GBps"],
                                 "bytes": calib["bytes"],
                                 "what": "torch copy_ (read + write counted) and fill_ of 2 GiB on this GPU"},

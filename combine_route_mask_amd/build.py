@@ -11,6 +11,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libmoe_ep.so")
 SOURCES = ["exchange.hip", "agrs.hip", "api.cpp"]
+# reference kernels of the benchmark (measurement only; the exchange never calls them)
+CEILINGS_LIB = os.path.join(HERE, "libmoe_ep_ceilings.so")
+CEILINGS_SOURCES = ["ceilings.hip"]
 
 # Packed-FP32 instructions are disabled for all device code.
 HIPCC_FLAGS = [
@@ -26,18 +29,24 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmoe_ep.so)")
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP/C++ source into libmoe_ep.so (always rebuilds)."""
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _compile(out: str, sources, verbose: bool) -> str:
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc(), *HIPCC_FLAGS, "-I", INCLUDE, "-I", CSRC, "-o", tmp,
-           *[os.path.join(CSRC, s) for s in SOURCES]]
+           *[os.path.join(CSRC, s) for s in sources]]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose: bool = False) -> str:
+    """Compile the exchange library libmoe_ep.so and the benchmark's
+    reference-kernel library libmoe_ep_ceilings.so (always rebuilds)."""
+    _compile(CEILINGS_LIB, CEILINGS_SOURCES, verbose)
+    return _compile(LIB, SOURCES, verbose)
 
 
 if __name__ == "__main__":

@@ -70,6 +70,27 @@ def test_trace_summary_context(tmp_path):
                    ("combine_bf16_kernel", "alone"): ("1", "41.0")}
 
 
+def test_trace_summary_reference_kernels(tmp_path):
+    """The plain reference kernels get their own "reference" rows and do not
+    change the exchange kernels' contexts."""
+    p = tmp_path / "trace.csv"
+    D, C = (DISPATCH, 1036 * 256), (COMBINE, 4096 * 256)
+    SC = ("void (anonymous namespace)::scatter_kernel(unsigned char const*, long, unsigned long const*, "
+          "unsigned long, long, unsigned char*, long)", 32768 * 256)
+    GA = ("void (anonymous namespace)::gather_kernel<true>(unsigned char const*, long, unsigned long const*, "
+          "unsigned long, long, long, unsigned char*)", 229376 * 256)
+    _trace(p, [(NORMAL, 2048 * 256, 500), (*D, 90000), (*D, 10000), (*D, 12000),
+               (*SC, 99000), (FLUSH, 1 << 26, 100000), (*SC, 30000),
+               (FLUSH, 1 << 26, 100000), (*SC, 32000), (*GA, 99000), (*GA, 25000),
+               (*D, 14000)])
+    lines = bench.trace_summary(str(p), ["wl"]).splitlines()
+    rows = [[c.strip() for c in l.split("|")[1:-1]] for l in lines[2:]]
+    got = {(r[1].strip("`"), r[3], r[4]): (r[2], r[5], r[6]) for r in rows}
+    assert got == {("dispatch_kernel<2, 4, true>", "warm", "alone"): ("1036", "3", "12.0"),
+                   ("scatter_kernel", "cold", "reference"): ("32768", "2", "31.0"),
+                   ("gather_kernel<true>", "warm", "reference"): ("229376", "1", "25.0")}
+
+
 def _pmc(path, entries):
     with open(path, "w", newline="") as f:
         w = csv.DictWriter(f, fieldnames=["Kernel_Name", "Grid_Size", "Counter_Value"])
@@ -117,3 +138,58 @@ def test_step_bytes_of_the_headline_workload():
     row, k, P, T = 14336, 8, 64, 512
     assert b["dispatch"] == N * k * 8 + N * row + M * (row + 8 * k) + (P * P * T - M) * 4 * k == 4154387904
     assert b["combine"] == M * 2 * 7168 + N * 2 * 7168
+
+
+def test_destination_masks_count_the_pairs():
+    """One bit per (token, destination rank) pair: popcounts add up to the
+    host pair count M, inactive rows and out-of-range ids set no bit."""
+    import numpy as np
+    import workloads as W
+    w = bench.WORKLOADS["ep64"]
+    R = W.draw_routing(w)
+    m = bench.destination_masks(w, R)
+    assert m.shape == (w.P * w.T,) and m.dtype == np.uint64
+    assert sum(bin(int(x)).count("1") for x in m) == bench.pair_count(w, R) == 251630
+    rows = m.reshape(w.P, w.T)
+    for s in (0, 17, 63):
+        assert not rows[s, R.counts[s]:].any()
+    # hand case: P = 4 ranks of 2 experts, k = 3
+    import dataclasses
+    w4 = dataclasses.replace(bench.WORKLOADS["ep8"], P=4, T=2, E=8, k=3)
+    R4 = W.Routing(np.array([2, 1, 1, 0], dtype=np.int32),
+                   np.array([[[0, 1, 7], [2, 9, -1]], [[3, 2, 4], [5, 5, 5]],
+                             [[6, 7, 0], [1, 1, 1]], [[8, 8, 8], [0, 0, 0]]], dtype=np.int32),
+                   np.zeros((4, 2, 3), np.float32))
+    got = bench.destination_masks(w4, R4).tolist()
+    assert got == [0b1001, 0b0010, 0b0110, 0, 0b1001, 0, 0, 0]
+
+
+def test_reference_kernels_reject_bad_sizes():
+    """The plain reference kernels check sizes on the host and return -1
+    before any launch (no GPU needed)."""
+    import ctypes as C
+    import os
+    if not os.path.exists(bench.CEILINGS_LIB):
+        from combine_route_mask_amd import build
+        build.build()
+    lib = bench.load_ceilings()
+    p = 4096  # never dereferenced: every call below fails its host checks
+    row = 14336
+    # source smaller than ntok rows
+    assert lib.ceil_scatter(p, row * 3, row, p, 4, 2, p, row * 4, row * 8, None) == -1
+    # destination: (nregions - 1) * region + ntok * row beyond the base
+    assert lib.ceil_scatter(p, row * 4, row, p, 4, 2, p, row * 4, row * 8 - 1, None) == -1
+    # rows the scatter cannot hold in its four vectors per lane, or ragged
+    assert lib.ceil_scatter(p, 1 << 30, 16400, p, 4, 2, p, 1 << 30, 1 << 31, None) == -1
+    assert lib.ceil_scatter(p, 1 << 30, row + 8, p, 4, 2, p, 1 << 30, 1 << 31, None) == -1
+    assert lib.ceil_scatter(p, row * 4, row, p, 4, 65, p, row * 4, 1 << 31, None) == -1
+    assert lib.ceil_scatter(None, row * 4, row, p, 4, 2, p, row * 4, row * 8, None) == -1
+    # gather: plane or output smaller than ntok rows, too many planes
+    assert lib.ceil_gather(p, row * 3, 2, p, 4, row, p, row * 4, 1, None) == -1
+    assert lib.ceil_gather(p, row * 4, 2, p, 4, row, p, row * 4 - 16, 1, None) == -1
+    assert lib.ceil_gather(p, row * 4, 65, p, 4, row, p, row * 4, 1, None) == -1
+    assert lib.ceil_gather(p, row * 4, 2, None, 4, row, p, row * 4, 1, None) == -1
+    # sweeps: too small, or a sink with fewer words than workgroups
+    assert lib.ceil_fill(p, 8, None) == -1
+    assert lib.ceil_read(p, 1 << 20, p, 16383, None) == -1
+    assert lib.ceil_read(p, 1 << 20, None, 16384, None) == -1
