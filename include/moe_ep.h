@@ -210,7 +210,8 @@ int moe_ep_dispatch(moe_ep_handle *h, const void *hidden, const void *scales,
  *                 (r*P*T + q)*H; only slots that received a token are read
  *  output         device [P][T][H] bf16: row t of rank s receives the sum
  *                 over ranks r that got token (s, t) of expert_output[r][s*T+t]
- *                 (fp32 accumulation, RNE to bf16); rows t >= n_s untouched
+ *                 (fp32 accumulation from +0 in ascending rank order, RNE to
+ *                 bf16); rows t >= n_s untouched
  * With MOE_EP_COMBINE_FP8 each sending rank first quantises its rows into
  * the source rank's landing plane (e4m3fn + e8m0 per 32), and the sum is
  * taken over the dequantised rows.
@@ -267,8 +268,8 @@ int moe_ep_allgatherv(int32_t ep_size, const int32_t *sizes, int32_t num_planes,
  * combine_into_output): rank q's full-length bf16 partial [sum(sizes)][H]
  * starts at in + q * in_rank_stride (bytes); rank r's result
  * [sizes[r]][H] at out + r * out_rank_stride (bytes) is the fp32 sum over
- * q of rows off_r .. off_r + sizes[r] - 1 (off_r = sum of sizes[q < r]),
- * rounded to bf16 (RNE).
+ * q (from +0, ascending q) of rows off_r .. off_r + sizes[r] - 1
+ * (off_r = sum of sizes[q < r]), rounded to bf16 (RNE).
  */
 int moe_ep_reduce_scatterv(int32_t ep_size, const int32_t *sizes, int32_t hidden_size,
                            const void *in, int64_t in_rank_stride, void *out,
