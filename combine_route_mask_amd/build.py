@@ -1,4 +1,6 @@
-"""Build the gfx950 HIP library ``libmoe_ep.so`` in-tree with hipcc."""
+"""Build the gfx950 HIP libraries in-tree with hipcc: ``libmoe_ep.so`` (the
+exchange behind include/moe_ep.h) and ``libmoe_ep_ceilings.so`` (the
+benchmark's plain reference kernels)."""
 from __future__ import annotations
 
 import os
