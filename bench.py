@@ -62,13 +62,19 @@ SOURCE_NAMES = ("exchange.hip", "agrs.hip", "formats.h", "memory_ops.h", "moe_ep
 KERNEL_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", f) for f in SOURCE_NAMES]
 
 
-def source_digest() -> str:
-    """Digest of the device sources with comments and blank space removed,
-    so that editing a comment does not retire the counter summaries."""
+# the benchmark's plain reference kernels (their own digest)
+REFERENCE_SOURCES = [os.path.join(ROOT, "combine_route_mask_amd", "csrc", "ceilings.hip")]
+REFERENCE_KERNELS = ("scatter_kernel", "gather_kernel", "fill_kernel", "read_kernel")
+
+
+def source_digest(paths=None) -> str:
+    """Digest of the device sources (default: the exchange's) with comments
+    and blank space removed, so that editing a comment does not retire the
+    counter summaries."""
     import hashlib
     import re
     h = hashlib.sha256()
-    for path in KERNEL_SOURCES:
+    for path in (KERNEL_SOURCES if paths is None else paths):
         text = open(path).read()
         text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
         text = re.sub(r"//[^\n]*", "", text)
@@ -76,17 +82,18 @@ def source_digest() -> str:
     return h.hexdigest()[:16]
 
 
-def measured_traffic(kernel: str, workload: str, config: str):
-    """HBM bytes per launch of `kernel` on `workload` from the committed
-    counter summary, or None when there is none or the kernel source has
-    changed since the counters were taken."""
+def measured_traffic(kernel: str, workload: str, config: str, instance=None):
+    """HBM bytes per launch of `kernel` (or of one `instance`) on `workload`
+    from the committed counter summary, or None when there is none or the
+    kernel source has changed since the counters were taken."""
     try:
         rows = [json.loads(l) for l in open(traffic_summary_path(config)) if l.startswith("{")]
     except OSError:
         return None
     for r in rows:
+        digest = source_digest(REFERENCE_SOURCES) if r.get("reference") else source_digest()
         if r.get("kernel") == kernel and r.get("workload") == workload and \
-                r.get("source_digest") == source_digest():
+                (instance is None or r.get("instance") == instance) and r.get("source_digest") == digest:
             return r["hbm_bytes_per_launch"]
     return None
 
@@ -102,7 +109,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
         per = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
             name = r["Kernel_Name"]
-            key = name.split("(anonymous namespace)::")[-1].split("(")[0] if "moe_ep" in name else name
+            key = name.split("(anonymous namespace)::")[-1].split("(")[0] \
+                if "(anonymous namespace)::" in name else name
             per[(key, int(r["Grid_Size"]))].append(float(r["Counter_Value"]))
         return per
 
@@ -116,16 +124,20 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
     family = ("allgatherv_kernel", "reduce_scatterv_kernel") if config == "agrs" else \
         ("dispatch_kernel", "combine_")
     for (k, g), vs in sorted(fetch.items()):
-        if not k.startswith(family):
+        ref = k.split("<")[0] in REFERENCE_KERNELS
+        if not (k.startswith(family) or ref):
             continue
         wv = write.get((k, g), [0.0])
         fk, wk = sum(vs) / len(vs), sum(wv) / len(wv)
-        lines.append(json.dumps({
-            "kernel": k.split("<")[0], "instance": k, "workload": workload, "grid_threads": g,
-            "fetch_KiB": round(fk, 1), "write_KiB": round(wk, 1),
-            "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
-            "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
-            "launches": len(vs), "source_digest": source_digest()}))
+        row = {"kernel": k.split("<")[0], "instance": k, "workload": workload, "grid_threads": g,
+               "fetch_KiB": round(fk, 1), "write_KiB": round(wk, 1),
+               "fetch_scale": round(f_scale, 4), "write_scale": round(w_scale, 4),
+               "hbm_bytes_per_launch": int(round((fk * f_scale + wk * w_scale) * 1024)),
+               "launches": len(vs)}
+        if ref:
+            row["reference"] = True
+        row["source_digest"] = source_digest(REFERENCE_SOURCES) if ref else source_digest()
+        lines.append(json.dumps(row))
     cfg = f" --config {config}"
     if config == "agrs":  # the AgRs step runs as an extra workload of another one
         run = ("python3 <repo>/bench.py --config ep8 --cache warm --also agrs --no-cpu-baseline --no-graph "
@@ -146,7 +158,8 @@ def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, co
                 "#       <out>/pmc_write/pmc_counter_collection.csv\n"
                 "# source_digest: first 16 hex digits of the sha256 of combine_route_mask_amd/csrc/\n"
                 f"# {', '.join(SOURCE_NAMES[:-1])} and {SOURCE_NAMES[-1]}, concatenated, with\n"
-                "# comments and white space removed\n")
+                "# comments and white space removed; rows marked \"reference\" are the bench's plain\n"
+                "# reference kernels (run on the headline workload's buffers), digest of csrc/ceilings.hip\n")
         for l in lines:
             f.write(l + "\n")
     return lines
@@ -477,7 +490,7 @@ def load_ceilings(path: str = CEILINGS_LIB):
     return lib
 
 
-def reference_kernels(setup, m, reps=5, flush_bytes=0):
+def reference_kernels(setup, m, reps=5, flush_bytes=0, config=None):
     """Plain reference kernels (libmoe_ep_ceilings.so) on the step's own
     buffers, each launch timed alone with HIP events on the launch stream
     (after the cache flush when flush_bytes): the dispatch's payload scatter
@@ -487,7 +500,9 @@ def reference_kernels(setup, m, reps=5, flush_bytes=0):
     buffer.  They move the exchange's bytes in its patterns with none of its
     routing work, so exchange / reference time is what that work costs on
     these allocations.  BF16 dispatch and combine only; run after the step's
-    own checks (the gather leaves truncated sums in the output)."""
+    own checks (the gather leaves truncated sums in the output).  With
+    config, each kernel's HBM bytes per launch from that workload's counter
+    summary ("traffic", null when none matches the current source)."""
     import ctypes as C
     import torch
     w = setup.w
@@ -542,6 +557,11 @@ def reference_kernels(setup, m, reps=5, flush_bytes=0):
         torch.cuda.synchronize()
         ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
         res[name] = {"us": ms * 1e3, "bytes": int(nbytes), "GBps": nbytes / (ms / 1e3) / 1e9}
+        inst = {"scatter": "scatter_kernel", "gather": "gather_kernel<true>",
+                "gather_reads_only": "gather_kernel<false>", "fill_workspace": "fill_kernel",
+                "read_expert_output": "read_kernel"}[name]
+        if config:
+            res[name]["traffic"] = measured_traffic(inst.split("<")[0], w.name, config, instance=inst)
     del flush
     res["dispatch_over_scatter"] = m["dispatch_ms"] * 1e3 / res["scatter"]["us"]
     res["combine_over_gather"] = m["combine_ms"] * 1e3 / res["gather"]["us"]
@@ -807,7 +827,7 @@ def main():
     ref_kernels = None
     if not args.no_reference_kernels:
         print(f"[bench] reference kernels on the {w.name} buffers", file=sys.stderr, flush=True)
-        ref_kernels = reference_kernels(setup, m, flush_bytes=(1 << 30) if cold else 0)
+        ref_kernels = reference_kernels(setup, m, flush_bytes=(1 << 30) if cold else 0, config=args.config)
     setup.free()
     torch.cuda.empty_cache()
     print(f"[bench] {w.name} ({args.cache}): {res['ms_per_step']*1e3:.1f} us/step", file=sys.stderr, flush=True)

@@ -116,6 +116,35 @@ def test_pmc_summary_scales_by_the_copy(tmp_path):
     assert open(out).read().count("\n{") == 1
 
 
+def test_pmc_summary_reference_kernels(tmp_path, monkeypatch):
+    """Reference-kernel rows carry their own source digest and are found by
+    kernel instance; an exchange row with the same grid is not confused with
+    them."""
+    copy_kib = (2 << 30) / 1024
+    fetch, write, out = tmp_path / "f.csv", tmp_path / "w.csv", tmp_path / "out.txt"
+    SC = ("void (anonymous namespace)::scatter_kernel(unsigned char const*, long, unsigned long const*, "
+          "unsigned long, long, unsigned char*, long)")
+    GT = ("void (anonymous namespace)::gather_kernel<true>(unsigned char const*, long, unsigned long const*, "
+          "unsigned long, long, long, unsigned char*)")
+    _pmc(fetch, [("__amd_rocclr_copyBuffer", 256, copy_kib / 2), (SC, 8388608, 100.0), (GT, 8388608, 400.0),
+                 (COMBINE, 8388608, 500.0)])
+    _pmc(write, [("__amd_rocclr_copyBuffer", 256, copy_kib), (SC, 8388608, 800.0), (GT, 8388608, 50.0),
+                 (COMBINE, 8388608, 60.0)])
+    lines = [json.loads(l) for l in bench.pmc_summary(str(fetch), str(write), str(out), "wl")]
+    by = {r["instance"]: r for r in lines}
+    assert set(by) == {"scatter_kernel", "gather_kernel<true>", "combine_bf16_kernel<1, 8, true>"}
+    assert by["scatter_kernel"]["reference"] and by["gather_kernel<true>"]["reference"]
+    assert "reference" not in by["combine_bf16_kernel<1, 8, true>"]
+    assert by["scatter_kernel"]["source_digest"] == bench.source_digest(bench.REFERENCE_SOURCES)
+    assert by["combine_bf16_kernel<1, 8, true>"]["source_digest"] == bench.source_digest()
+    assert by["scatter_kernel"]["hbm_bytes_per_launch"] == int(round((100.0 * 2 + 800.0) * 1024))
+    monkeypatch.setattr(bench, "traffic_summary_path", lambda config: str(out))
+    assert bench.measured_traffic("gather_kernel", "wl", "x", instance="gather_kernel<true>") == \
+        int(round((400.0 * 2 + 50.0) * 1024))
+    assert bench.measured_traffic("gather_kernel", "wl", "x", instance="gather_kernel<false>") is None
+    assert bench.measured_traffic("combine_bf16_kernel", "wl", "x") == int(round((500.0 * 2 + 60.0) * 1024))
+
+
 def test_also_plan_cache_states():
     """--also entries are warm unless suffixed '-cold'; the headline in its own
     cache state is not repeated; warm and cold runs of one workload share one
