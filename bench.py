@@ -642,6 +642,73 @@ def trace_summary(trace_csv: str, workloads: list) -> str:
     return "\n".join(out) + "\n"
 
 
+def pmc_table(counter_csv: str, workloads: list) -> str:
+    """Markdown table of per-launch counter means from a rocprofv3 counter
+    run of the bench (any counters), grouped like trace_summary: workload
+    phase, exchange or reference kernel instance, cache state (a launch
+    after a 1 GiB flush is cold); the first launch of an instance in a
+    workload is left out; "mean us" from the dispatches' timestamps.  With
+    TCC_EA0_WRREQ_sum, the ratios of TCC_EA0_WRREQ_STALL_sum (stalled cycles
+    per write request) and of TCC_EA0_WRREQ_LEVEL_sum (requests in flight
+    summed per cycle: the mean write latency in cycles) to it are added; with
+    TCP_TCC_WRITE_REQ_sum, the mean L1-to-L2 write latency
+    (TCP_TCC_WRITE_REQ_LATENCY_sum / TCP_TCC_WRITE_REQ_sum); with
+    GRBM_GUI_ACTIVE, the busy fraction of the second-level translation cache
+    (GRBM_UTCL2_BUSY / GRBM_GUI_ACTIVE)."""
+    import collections
+    import csv
+    import re
+    ours = ("dispatch_kernel", "combine_bf16_kernel", "combine_fp8_quant_kernel",
+            "combine_fp8_gather_kernel", "allgatherv_kernel", "reduce_scatterv_kernel") + REFERENCE_KERNELS
+    disp = collections.OrderedDict()
+    for r in csv.DictReader(open(counter_csv)):
+        d = disp.setdefault(int(r["Dispatch_Id"]), {"name": r["Kernel_Name"], "grid": int(r["Grid_Size"]),
+                                                    "c": {}})
+        if r.get("End_Timestamp") and r.get("Start_Timestamp"):
+            d["us"] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        d["c"][r["Counter_Name"]] = d["c"].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    counters = sorted({k for d in disp.values() for k in d["c"]})
+    phase, ran, after_flush, seen = 0, False, False, set()
+    groups = collections.defaultdict(list)
+    for _, d in sorted(disp.items()):
+        name = d["name"]
+        if "normal_kernel" in name and ran:
+            phase, ran = phase + 1, False
+            continue
+        if "FillFunctor<unsigned char>" in name and d["grid"] >= (1 << 26):
+            after_flush = True
+            continue
+        m = re.search(r"(\w+_kernel(<[^(]*>)?)\(", name)
+        if not m or m.group(1).split("<")[0] not in ours:
+            continue
+        inst, cold, after_flush = m.group(1), after_flush, False
+        if inst.split("<")[0] not in REFERENCE_KERNELS:
+            ran = True
+        if (phase, inst) not in seen:
+            seen.add((phase, inst))
+            continue
+        groups[(phase, inst, "cold" if cold else "warm")].append(dict(d["c"], _us=d.get("us", 0.0)))
+    extra = []
+    if "TCC_EA0_WRREQ_sum" in counters:
+        extra = [x for x in ("TCC_EA0_WRREQ_STALL_sum", "TCC_EA0_WRREQ_LEVEL_sum") if x in counters]
+    if "TCP_TCC_WRITE_REQ_sum" in counters and "TCP_TCC_WRITE_REQ_LATENCY_sum" in counters:
+        extra.append("TCP_TCC_WRITE_REQ_LATENCY_sum")
+    ratio_to = {x: ("TCP_TCC_WRITE_REQ_sum" if x.startswith("TCP_") else "TCC_EA0_WRREQ_sum") for x in extra}
+    if "GRBM_UTCL2_BUSY" in counters and "GRBM_GUI_ACTIVE" in counters:
+        extra.append("GRBM_UTCL2_BUSY")
+        ratio_to["GRBM_UTCL2_BUSY"] = "GRBM_GUI_ACTIVE"
+    head = ["workload", "kernel", "cache", "launches", "mean us"] + counters + \
+        [f"{x} / {ratio_to[x]}" for x in extra]
+    out = ["| " + " | ".join(head) + " |", "|" + "---|" * len(head)]
+    for (ph, inst, c), ds in sorted(groups.items()):
+        label = workloads[ph] if ph < len(workloads) else str(ph)
+        mean = {k: sum(d.get(k, 0.0) for d in ds) / len(ds) for k in counters + ["_us"]}
+        cells = [label, f"`{inst}`", c, str(len(ds)), f"{mean['_us']:.1f}"] + [f"{mean[k]:.4g}" for k in counters]
+        cells += [f"{mean[x] / mean[ratio_to[x]]:.3g}" if mean[ratio_to[x]] else "-" for x in extra]
+        out.append("| " + " | ".join(cells) + " |")
+    return "\n".join(out) + "\n"
+
+
 def calibrate(nbytes=2 << 30, iters=10):
     """Achievable HBM bandwidth on this GPU: a plain device copy (read +
     write, torch copy_) and a fill (write only) of nbytes."""
@@ -787,6 +854,9 @@ def main():
                          "of this bench (same --config / --cache / --also) and exit")
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the counter traffic summary under profiles/ and exit")
+    ap.add_argument("--pmc-table", metavar="COUNTER_CSV",
+                    help="print the per-workload counter table of a rocprofv3 counter run of this bench "
+                         "(same --config / --cache / --also) and exit")
     args = ap.parse_args()
     cold = args.cache == "cold"
     if args.trace_summary:
@@ -794,6 +864,12 @@ def main():
         for base, colds in also_plan(args).items():
             labels.append(base if False in colds else base + "-cold")
         print(trace_summary(args.trace_summary, labels), end="")
+        return
+    if args.pmc_table:
+        labels = [args.config + ("-cold" if cold else "")]
+        for base, colds in also_plan(args).items():
+            labels.append(base if False in colds else base + "-cold")
+        print(pmc_table(args.pmc_table, labels), end="")
         return
     if args.pmc_summary:
         for l in pmc_summary(*args.pmc_summary, traffic_summary_path(args.config),

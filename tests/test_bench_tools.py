@@ -145,6 +145,42 @@ def test_pmc_summary_reference_kernels(tmp_path, monkeypatch):
     assert bench.measured_traffic("combine_bf16_kernel", "wl", "x") == int(round((500.0 * 2 + 60.0) * 1024))
 
 
+def test_pmc_table_phases_and_ratios(tmp_path):
+    """Counter rows of one dispatch are merged; workloads split at the first
+    random-input kernel after exchange kernels; the reference kernels do not
+    start a workload; cold after a flush; ratios to the write requests."""
+    p = tmp_path / "ctr.csv"
+    cols = ["Dispatch_Id", "Grid_Size", "Kernel_Name", "Counter_Name", "Counter_Value"]
+    SC = ("void (anonymous namespace)::scatter_kernel(unsigned char const*, long, unsigned long const*, "
+          "unsigned long, long, unsigned char*, long)")
+    seq = [(NORMAL, 1), (DISPATCH, 1), (FLUSH, 1 << 26), (DISPATCH, 1), (FLUSH, 1 << 26), (DISPATCH, 1),
+           (SC, 1), (SC, 1), (NORMAL, 1), (DISPATCH, 1), (DISPATCH, 1)]
+    vals = {1: (10, 5, 40), 3: (100, 50, 400), 5: (100, 150, 600), 6: (7, 7, 7), 7: (80, 8, 160),
+            9: (1, 1, 1), 10: (20, 10, 60)}
+    with open(p, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        for i, (name, grid) in enumerate(seq):
+            wr, st, lv = vals.get(i, (0, 0, 0))
+            for cn, cv in (("TCC_EA0_WRREQ_sum", wr), ("TCC_EA0_WRREQ_STALL_sum", st),
+                           ("TCC_EA0_WRREQ_LEVEL_sum", lv)):
+                w.writerow({"Dispatch_Id": i + 1, "Grid_Size": grid * 256, "Kernel_Name": name,
+                            "Counter_Name": cn, "Counter_Value": cv})
+    lines = bench.pmc_table(str(p), ["first", "second"]).splitlines()
+    head = [c.strip() for c in lines[0].split("|")[1:-1]]
+    assert head[-2:] == ["TCC_EA0_WRREQ_STALL_sum / TCC_EA0_WRREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum / TCC_EA0_WRREQ_sum"]
+    rows = {(r[0], r[1].strip("`"), r[2]): r for r in
+            ([c.strip() for c in l.split("|")[1:-1]] for l in lines[2:])}
+    # first workload: dispatches 3 and 5 (cold; 1 is its warm-up), scatter 7 (warm; 6 is its warm-up);
+    # second: dispatch 10 (9 is its warm-up)
+    d = rows[("first", "dispatch_kernel<2, 4, true>", "cold")]
+    assert d[3] == "2" and d[-2] == "1" and d[-1] == "5" and d[4] == "0.0"
+    sc = rows[("first", "scatter_kernel", "warm")]
+    assert sc[3] == "1" and sc[-2] == "0.1" and sc[-1] == "2"
+    d2 = rows[("second", "dispatch_kernel<2, 4, true>", "warm")]
+    assert d2[3] == "1" and d2[-2] == "0.5" and d2[-1] == "3"
+
+
 def test_also_plan_cache_states():
     """--also entries are warm unless suffixed '-cold'; the headline in its own
     cache state is not repeated; warm and cold runs of one workload share one
