@@ -27,11 +27,18 @@ line:
                without stores, whole-buffer fill and read), timed like the
                step's launches: what its routing work costs over them
   also         the other workloads (--also), warm, or cold with a '-cold'
-               suffix
+               suffix; by default EP64 warm, EP8 warm and cold, EP64 NVFP4,
+               the MXFP8 workload with FP8 combine, EP64 DeepSeekFp8, EP64
+               NVFP4 with 1 KB router logits per token and 256 EPLB
+               statistics per rank, EP64 with 48 of 64 ranks taking part,
+               and AgRs
 
-Algorithmic bytes (per launch; N tokens, M (token, destination) pairs,
-row / srow payload and scale row bytes, k, P ranks, T tokens per rank):
-  dispatch  N*k*8 + N*(row+srow) + M*(row+srow+8k) + (P*P*T - M)*4k
+Algorithmic bytes (per launch; N tokens of the ranks taking part, M
+(token, destination) pairs between them, row / srow payload (with its extra
+bytes) and scale row bytes, k, P ranks of which L take part, T tokens per
+rank, n EPLB statistics per rank):
+  dispatch  N*k*8 + N*(row+srow) + M*(row+srow+8k) + (L*P*T - M)*4k
+            + L*n*4 + L*L*n*4
   combine   bf16: M*2H + N*2H
             fp8:  quantise M*(2H + H + H/32), gather M*(H + H/32) + N*2H
 """
@@ -169,18 +176,38 @@ WORKLOADS = {
     "ep8-mxfp8": W.EP8_MXFP8,
     "ep64": W.EP64_BF16,
     "ep64-nvfp4": W.EP64_NVFP4,
+    "ep64-dsfp8": W.EP64_DSFP8,
+    "ep64-nvfp4-extras": W.EP64_NVFP4_EXTRAS,
+    "ep64-alive48": W.EP64_MASK48,
     "agrs": W.AGRS16,
 }
 
 
+def live_ranks(w) -> np.ndarray:
+    """[P] bool: the ranks that take part in the step (all unless w.alive)."""
+    live = np.zeros(w.P, bool)
+    live[list(range(w.P)) if w.alive is None else list(w.alive)] = True
+    return live
+
+
+def live_tokens(w, R) -> int:
+    """N: tokens of the ranks that take part (masked-off ranks send nothing)."""
+    return int(np.asarray(R.counts)[live_ranks(w)].sum())
+
+
 def pair_count(w, R) -> int:
     """M: distinct (token, destination rank) pairs, from the routing on the
-    host (numpy; ids outside [0, E) route nowhere)."""
+    host (numpy; ids outside [0, E) route nowhere; only ranks that take part
+    send and receive)."""
     M = 0
     epr = w.E // w.P
+    live = live_ranks(w)
     for s in range(w.P):
+        if not live[s]:
+            continue
         ids = R.ids[s, :R.counts[s]]
         own = np.where((ids >= 0) & (ids < w.E), ids // epr, -1)
+        own = np.where(live[np.clip(own, 0, w.P - 1)], own, -1)
         own = np.sort(own, axis=1)
         distinct = (own[:, 1:] != own[:, :-1]) & (own[:, 1:] >= 0)
         M += int(distinct.sum() + (own[:, 0] >= 0).sum())
@@ -188,10 +215,13 @@ def pair_count(w, R) -> int:
 
 
 def step_bytes(w, N, M):
-    row = W.payload_row_bytes(w.fmt, w.H)
+    row = W.payload_row_bytes(w.fmt, w.H) + w.extra_bytes  # extra bytes travel with the row
     srow = W.scale_row_bytes(w.fmt, w.H)
     k, P, T, H = w.k, w.P, w.T, w.H
-    disp = N * k * 8 + N * (row + srow) + M * (row + srow + 8 * k) + (P * P * T - M) * 4 * k
+    L = int(live_ranks(w).sum())
+    disp = N * k * 8 + N * (row + srow) + M * (row + srow + 8 * k) + (L * P * T - M) * 4 * k
+    # EPLB statistics: each live rank's row read once, the live rows written to every live region
+    disp += L * w.n_eplb * 4 + L * L * w.n_eplb * 4
     if w.combine == "fp8":
         quant = M * (2 * H + H + H // 32)
         gather = M * (H + H // 32) + N * 2 * H
@@ -220,23 +250,28 @@ class Setup:
         self.weights = torch.from_numpy(self.R.weights).to(dev)
         del d
         self.eo = W.draw_expert_output(w.P, w.T, w.H, w.seed, device=dev)
+        self.extra, self.stats = W.draw_extras(w, device=dev, seed=seed)
         self.ex = MoeEpExchange(w.P, w.E, w.k, w.T, w.H, dispatch_format=w.fmt,
-                                combine_format=w.combine, device=dev)
+                                combine_format=w.combine, extra_payload_bytes_per_token=w.extra_bytes,
+                                eplb_stats_num_experts=w.n_eplb, device=dev)
         self.out = torch.empty((w.P, w.T, w.H), dtype=torch.bfloat16, device=dev)
         self.counts = self.R.counts.tolist()
-        self.N = int(self.R.counts.sum())
+        self.N = live_tokens(w, self.R)
         self.M = pair_count(w, self.R)
+        mask = None if w.alive is None else sum(1 << r for r in w.alive)
         # first step through the checked binding (sets up the views)
         self.views = self.ex.dispatch(self.payload, self.ids, self.weights, scales=self.scales,
-                                      num_tokens=self.counts, runtime_max_tokens_per_rank=w.T)
+                                      num_tokens=self.counts, runtime_max_tokens_per_rank=w.T,
+                                      active_rank_mask=mask, extra_payload=self.extra,
+                                      eplb_local_stats=self.stats)
         self.ex.combine(self.eo, self.out)
         self._lib = moe_ep.lib
         self._h = self.ex.handle
-        self._args = (C.c_void_p(self.payload.data_ptr()),
-                      C.c_void_p(self.scales.data_ptr()) if self.scales is not None else None,
-                      None, None,
-                      C.c_void_p(self.ids.data_ptr()), C.c_void_p(self.weights.data_ptr()),
-                      (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T), None)
+        ptr = lambda t: C.c_void_p(t.data_ptr()) if t is not None else None
+        self._mask = None if mask is None else (C.c_uint64 * 1)(mask)
+        self._args = (ptr(self.payload), ptr(self.scales), ptr(self.extra), ptr(self.stats),
+                      ptr(self.ids), ptr(self.weights),
+                      (C.c_int32 * w.P)(*self.counts), C.c_int32(w.T), self._mask)
         self._eo = C.c_void_p(self.eo.data_ptr())
         self._out = C.c_void_p(self.out.data_ptr())
 
@@ -256,7 +291,7 @@ class Setup:
 
     def free(self):
         self.ex.destroy()
-        del self.eo, self.payload, self.ex, self.views
+        del self.eo, self.payload, self.ex, self.views, self.extra, self.stats
 
 
 class AgRsSetup:
@@ -377,8 +412,10 @@ def measure(setup, steps, warmup, flush_bytes=0, graphs=True, check=True):
     torch.cuda.synchronize()
     exchange = isinstance(setup, Setup) and check
     if exchange:
-        # the step's receive counts must match the host-side pair count
-        got_M = int(setup.views["counts"].sum().item())
+        # the step's receive counts (regions that take part; the others are
+        # never written) must match the host-side pair count
+        live = torch.from_numpy(live_ranks(setup.w)).to(setup.views["counts"].device)
+        got_M = int(setup.views["counts"][live].sum().item())
         assert got_M == setup.M, (got_M, setup.M)
         ref_out = setup.out.clone()
         ref_ids = setup.views["ids"].clone()
@@ -465,15 +502,18 @@ CEILINGS_LIB = os.path.join(ROOT, "combine_route_mask_amd", "libmoe_ep_ceilings.
 def destination_masks(w, R) -> np.ndarray:
     """[P*T] uint64, entry s*T + t: bit r set when token t of rank s has an
     expert on rank r (contiguous ownership, E/P experts per rank; ids outside
-    [0, E) route nowhere); 0 for rows t >= n_s.  Popcounts sum to M."""
+    [0, E) route nowhere) and both ranks take part; 0 for rows t >= n_s.
+    Popcounts sum to M."""
     assert w.P <= 64
     epr = w.E // w.P
+    live = live_ranks(w)
     ids = R.ids.astype(np.int64)
-    valid = (ids >= 0) & (ids < w.E)
-    owner = np.where(valid, ids, 0) // epr
+    owner = np.where((ids >= 0) & (ids < w.E), ids, 0) // epr
+    valid = (ids >= 0) & (ids < w.E) & live[owner]
     bits = np.where(valid, np.left_shift(np.uint64(1), owner.astype(np.uint64)), np.uint64(0))
     m = np.bitwise_or.reduce(bits, axis=2)
     m[np.arange(w.T)[None, :] >= np.asarray(R.counts)[:, None]] = 0
+    m[~live] = 0
     return m.reshape(-1)
 
 
@@ -506,7 +546,7 @@ def reference_kernels(setup, m, reps=5, flush_bytes=0, config=None):
     import ctypes as C
     import torch
     w = setup.w
-    if w.fmt != "bf16" or w.combine != "bf16" or w.P > 64:
+    if w.fmt != "bf16" or w.combine != "bf16" or w.P > 64 or w.extra_bytes or w.n_eplb:
         return None
     try:
         lib = load_ceilings()
@@ -773,8 +813,11 @@ def cpu_baseline(w, budget_s=12.0):
     R = d.routing
     payload = d.payload.numpy()
     scales = None if d.scales is None else d.scales.numpy()
-    N = int(R.counts.sum())
+    N = live_tokens(w, R)
     P, T = w.P, w.T
+    active = None if w.alive is None else sum(1 << r for r in w.alive)
+    extra, _ = W.draw_extras(w, device="cpu")
+    extra = None if extra is None else extra.numpy()
     g = W.torch_generator(w.seed + 7, "cpu")
     eo_s = W.normal_bf16((P, T, w.H), g, "cpu").view(torch.int16).numpy().view(np.uint16)
     t_disp, t_comb = [], []
@@ -782,13 +825,14 @@ def cpu_baseline(w, budget_s=12.0):
     while sum(t_disp) + sum(t_comb) < budget_s or not (t_disp and t_comb):
         r = (i * 37) % P  # spread the sampled ranks
         a = time.perf_counter()
-        oracle.dispatch(R.counts, payload, R.ids, R.weights, scales, E=w.E, r0=r, r1=r + 1)
+        oracle.dispatch(R.counts, payload, R.ids, R.weights, scales, E=w.E, r0=r, r1=r + 1, active=active,
+                        extra=extra)
         t_disp.append(time.perf_counter() - a)
         a = time.perf_counter()
         if w.combine == "fp8":
-            oracle.combine_fp8(R.counts, R.ids, eo_s, E=w.E, s0=r, s1=r + 1, slot0=r * T)
+            oracle.combine_fp8(R.counts, R.ids, eo_s, E=w.E, s0=r, s1=r + 1, slot0=r * T, active=active)
         else:
-            oracle.combine_bf16(R.counts, R.ids, eo_s, E=w.E, s0=r, s1=r + 1, slot0=r * T)
+            oracle.combine_bf16(R.counts, R.ids, eo_s, E=w.E, s0=r, s1=r + 1, slot0=r * T, active=active)
         t_comb.append(time.perf_counter() - a)
         i += 1
     el = sum(t_disp) + sum(t_comb)
@@ -841,7 +885,8 @@ def main():
     ap.add_argument("--cache", default="cold", choices=("cold", "warm"),
                     help="cold (default): write 1 GiB and read another 1 GiB before every timed step and "
                          "launch of the headline workload, so the last-level cache holds none of its data")
-    ap.add_argument("--also", default="ep64,ep8,ep8-cold,ep64-nvfp4,ep8-mxfp8,agrs",
+    ap.add_argument("--also", default="ep64,ep8,ep8-cold,ep64-nvfp4,ep8-mxfp8,ep64-dsfp8,ep64-nvfp4-extras,"
+                                      "ep64-alive48,agrs",
                     help="comma list of extra workloads ('' for none), warm unless suffixed '-cold'")
     ap.add_argument("--no-graph", action="store_true",
                     help="time eager launches only (for counter-collection runs)")

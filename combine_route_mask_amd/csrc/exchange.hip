@@ -43,6 +43,14 @@
 #ifndef MOE_EP_DISPATCH_LONG_ROW
 #define MOE_EP_DISPATCH_LONG_ROW 8192
 #endif
+// Short rows in launches too large to prefetch (below) take this many
+// vectors per thread instead: a row of up to 8 KB per workgroup, so each
+// token's mask is built once.  EP64 DeepSeekFp8 dispatch (7 KB rows, same
+// buffers) 481 -> 429 us, EP64 NVFP4 (3.5 KB rows) 217 -> 216 us; the
+// prefetching MXFP8 dispatch keeps 1 (2 there: +7%).
+#ifndef MOE_EP_DISPATCH_VPT_MID
+#define MOE_EP_DISPATCH_VPT_MID 2
+#endif
 // Dispatches of at most this many (token, row chunk) items, eight rounds of
 // resident workgroups, load each row before its token's mask.
 #ifndef MOE_EP_PREFETCH_ITEMS
@@ -893,8 +901,11 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     int64_t plane_blocks = grid_for(ceil_div(a.P, kPlaneGroup) * nplane);
     const bool long_rows = a.row_bytes >= MOE_EP_DISPATCH_LONG_ROW;
     const int dv = long_rows ? MOE_EP_DISPATCH_VPT_LONG : MOE_EP_DISPATCH_VPT_SHORT;
-    const int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
+    int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
     const bool pf = S * nchunk <= MOE_EP_PREFETCH_ITEMS;
+    const bool mid = !long_rows && !pf; // short rows, large launch
+    if (mid)
+        nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * MOE_EP_DISPATCH_VPT_MID);
     int64_t N = 0;
     for (int i = 0; i < a.P; ++i)
         N += a.n[i];
@@ -917,7 +928,7 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     // extra rows that fit one word per lane travel with the payload loads
     const bool xf = side_row_fits(a.extra, a.xrow_bytes, a.off_extra, a.region);
     const dim3 g((unsigned)grid);
-    constexpr int L = MOE_EP_DISPATCH_VPT_LONG, Sh = MOE_EP_DISPATCH_VPT_SHORT;
+    constexpr int L = MOE_EP_DISPATCH_VPT_LONG, Sh = MOE_EP_DISPATCH_VPT_SHORT, Md = MOE_EP_DISPATCH_VPT_MID;
     if (long_rows && pf && wt)
         launch_dispatch_xf<KQ, L, true, true>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (long_rows && pf)
@@ -929,7 +940,7 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     else if (pf)
         launch_dispatch_xf<KQ, Sh, true, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else
-        launch_dispatch_xf<KQ, Sh, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
+        launch_dispatch_xf<KQ, Md, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     return hipGetLastError();
 }
 

@@ -2,7 +2,9 @@
 tokens per rank, hidden 7168, 256 experts, top-8), in the launch
 configuration the bench times: every destination's receive planes
 (payload, scale, id and weight planes, counts, source offsets, slot
-lists) bit-exact for BF16 and NVFP4 dispatch, every token of the BF16
+lists) bit-exact for BF16, NVFP4 and DeepSeekFp8 dispatch and for NVFP4
+with 1 KB of router logits per token, 256 EPLB statistics per rank and 48
+of the 64 ranks taking part, every token of the BF16
 combine against the oracle's fp32 sum (NaN in every expert-output slot
 that received no token), and the identity-expert invariant over all 32768
 tokens.  The oracle takes one destination, or one source rank's slots, at
@@ -164,3 +166,66 @@ def test_ep64_nvfp4_dispatch_every_destination():
         _check_destinations(st, 0, st.w.P)
     finally:
         st.free()
+
+
+def test_ep64_deepseek_fp8_dispatch_every_destination():
+    """7 KB DeepSeekFp8 rows in a launch too large to prefetch: two vectors
+    per lane, one workgroup per row (the EP64 DeepSeekFp8 workload)."""
+    st = Step(W.EP64_DSFP8)
+    try:
+        _check_bookkeeping(st)
+        _check_destinations(st, 0, st.w.P)
+    finally:
+        st.free()
+
+
+def test_ep64_nvfp4_extras_alive48_every_destination():
+    """The bench's EP64 NVFP4 workload with each token's 1 KB of router
+    logits (extra payload, loaded with the row), 256 EPLB statistics per
+    rank, and 48 of the 64 ranks taking part: every live destination's
+    payload, scale, extra, id and weight rows and gathered statistics
+    bit-exact; the 16 masked-off regions untouched (poisoned workspace)."""
+    import dataclasses
+    from combine_route_mask_amd.moe_ep import MoeEpExchange
+    w = dataclasses.replace(W.EP64_NVFP4_EXTRAS, alive=W.EP64_MASK48.alive)
+    log(f"ep64 setup: {w.name} alive48")
+    c = random_byte_case(w, w.seed)
+    rng = np.random.default_rng(w.seed + 17)
+    extra = rng.integers(0, 256, size=(w.P, w.T, w.extra_bytes)).astype(np.uint8)
+    stats = rng.integers(-(1 << 30), 1 << 30, size=(w.P, w.n_eplb)).astype(np.int32)
+    live = list(w.alive)
+    active = sum(1 << r for r in live)
+    ex = MoeEpExchange(w.P, w.E, w.k, w.T, w.H, dispatch_format=w.fmt, combine_format=w.combine,
+                       extra_payload_bytes_per_token=w.extra_bytes, eplb_stats_num_experts=w.n_eplb)
+    try:
+        ex.workspace.fill_(0x5A)
+        pl = torch.from_numpy(c.payload).cuda()
+        sc = torch.from_numpy(c.scales).cuda()
+        out = ex.dispatch(pl, torch.from_numpy(c.ids).cuda(), torch.from_numpy(c.weights).cuda(), scales=sc,
+                          num_tokens=c.counts.tolist(), runtime_max_tokens_per_rank=w.T, active_rank_mask=active,
+                          extra_payload=torch.from_numpy(extra).cuda(), eplb_local_stats=torch.from_numpy(stats).cuda())
+        torch.cuda.synchronize()
+        for r in range(w.P):
+            if r not in live:
+                assert bool((ex.workspace[r] == 0x5A).all()), f"masked-off rank {r} was written"
+        g = out["eplb_gathered_stats"].cpu().numpy()
+        poison = np.full((w.P, w.n_eplb), 0x5A5A5A5A, np.int32)
+        ids_g = out["ids"]
+        for r in live:
+            one = oracle.dispatch(c.counts, c.payload, c.ids, c.weights, c.scales, E=w.E, r0=r, r1=r + 1,
+                                  active=active, extra=extra)
+            v = one["valid"][0].astype(bool)
+            assert np.array_equal(ids_g[r].cpu().numpy(), one["ids"][0]), f"ids plane of rank {r}"
+            idx = torch.from_numpy(np.nonzero(v)[0]).cuda()
+            for key in ("payload", "scales", "extra"):
+                assert np.array_equal(out[key][r].index_select(0, idx).cpu().numpy(), one[key][0][v]), \
+                    f"{key} of rank {r} differs"
+            wt = out["weights"][r].index_select(0, idx).cpu().numpy()
+            assert np.array_equal(wt.view(np.uint32), one["weights"][0][v].view(np.uint32)), f"weights of rank {r}"
+            expect = oracle.eplb_allgather(stats, r, active=active, out=poison.copy())
+            assert np.array_equal(g[r], expect), f"gathered statistics of rank {r}"
+        log(f"{w.name}: 48 live destinations bit-exact, 16 masked-off regions untouched")
+    finally:
+        ex.destroy()
+        del ex
+        torch.cuda.empty_cache()

@@ -43,6 +43,9 @@ class Workload:
     token counts (inclusive, uniform).  ``routing`` is ``"uniform"``
     (k distinct experts uniformly) or ``"zipf"`` (k distinct experts,
     popularity p_e proportional to (e+1)^-zipf_s, drawn by Gumbel-top-k).
+    ``extra_bytes`` more bytes per token travel with the payload (router
+    logits: E fp32 values), ``n_eplb`` per-expert int32 statistics per rank
+    are all-gathered, and only the ranks in ``alive`` take part (None: all).
     """
 
     name: str
@@ -58,6 +61,9 @@ class Workload:
     routing: str = "uniform"
     zipf_s: float = 1.2
     seed: int = 0
+    extra_bytes: int = 0
+    n_eplb: int = 0
+    alive: Optional[tuple] = None
 
     @property
     def epr(self) -> int:
@@ -76,6 +82,15 @@ EP64_BF16 = Workload("ep64 T512 H7168 bf16 E256 k8", P=64, T=512, H=7168,
                      E=256, k=8, n_lo=512, n_hi=512, seed=4)
 EP64_NVFP4 = dataclasses.replace(EP64_BF16, name="ep64 T512 H7168 nvfp4 E256 k8",
                                  fmt=FMT_NVFP4)
+# The next rows on the EP64 shape: DeepSeekFp8 payloads; NVFP4 with each
+# token's 256 fp32 router logits as extra payload and 256 per-expert
+# statistics all-gathered; BF16 with 48 of the 64 ranks taking part.
+EP64_DSFP8 = dataclasses.replace(EP64_BF16, name="ep64 T512 H7168 deepseek_fp8 E256 k8",
+                                 fmt=FMT_DEEPSEEK_FP8)
+EP64_NVFP4_EXTRAS = dataclasses.replace(EP64_NVFP4, name="ep64 T512 H7168 nvfp4 E256 k8 logits1024 eplb256",
+                                        extra_bytes=1024, n_eplb=256)
+EP64_MASK48 = dataclasses.replace(EP64_BF16, name="ep64 T512 H7168 bf16 E256 k8 alive48",
+                                  alive=tuple(r for r in range(64) if r % 4 != 3))
 
 
 @dataclasses.dataclass(frozen=True)
@@ -280,6 +295,25 @@ class DispatchInputs:
     payload: object        # torch uint8/bf16 tensor [P, T, row_bytes] (as bytes view)
     scales: object         # torch uint8 [P, T, scale_row_bytes] or None
     hidden_bf16: object    # the bf16 rows the payload was encoded from [P, T, H]
+
+
+def draw_extras(w: Workload, device="cpu", seed: Optional[int] = None):
+    """(extra payload uint8 [P, T, extra_bytes] or None, EPLB statistics
+    int32 [P, n_eplb] or None).  The extra rows are the bytes of N(0,1)
+    fp32 values (router logits); the statistics are per-expert token
+    counts drawn uniformly in [0, 4T]."""
+    torch = _torch()
+    seed = w.seed if seed is None else seed
+    extra = stats = None
+    if w.extra_bytes:
+        g = torch_generator(seed + 7919, device)
+        nf = (w.extra_bytes + 3) // 4
+        x = torch.randn((w.P, w.T, nf), generator=g, device=device, dtype=torch.float32)
+        extra = x.view(torch.uint8)[..., :w.extra_bytes].contiguous()
+    if w.n_eplb:
+        rng = np.random.default_rng(seed + 104729)
+        stats = torch.from_numpy(rng.integers(0, 4 * w.T + 1, size=(w.P, w.n_eplb)).astype(np.int32)).to(device)
+    return extra, stats
 
 
 def draw_dispatch_inputs(w: Workload, device="cpu", seed: Optional[int] = None,
