@@ -43,11 +43,14 @@
 #ifndef MOE_EP_DISPATCH_LONG_ROW
 #define MOE_EP_DISPATCH_LONG_ROW 8192
 #endif
-// Short rows in launches too large to prefetch (below) take this many
-// vectors per thread instead: a row of up to 8 KB per workgroup, so each
-// token's mask is built once.  EP64 DeepSeekFp8 dispatch (7 KB rows, same
-// buffers) 481 -> 429 us, EP64 NVFP4 (3.5 KB rows) 217 -> 216 us; the
-// prefetching MXFP8 dispatch keeps 1 (2 there: +7%).
+// Short rows longer than one chunk (4 KB) in launches too large to prefetch
+// (below) take this many vectors per thread instead: a row of up to 8 KB
+// per workgroup, so each token's mask is built once.  EP64 DeepSeekFp8
+// dispatch (7 KB rows, same buffers) 481 -> 429 us; the prefetching MXFP8
+// dispatch keeps 1 (2 there: +7%).  Rows of one chunk keep 1: the split is
+// the same, and with 1 KB of extra payload loaded beside the row the EP64
+// NVFP4 dispatch took 298 us with 2 against 291 with 1 (without extras
+// 216 / 220 us).
 #ifndef MOE_EP_DISPATCH_VPT_MID
 #define MOE_EP_DISPATCH_VPT_MID 2
 #endif
@@ -903,7 +906,7 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
     const int dv = long_rows ? MOE_EP_DISPATCH_VPT_LONG : MOE_EP_DISPATCH_VPT_SHORT;
     int64_t nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * dv);
     const bool pf = S * nchunk <= MOE_EP_PREFETCH_ITEMS;
-    const bool mid = !long_rows && !pf; // short rows, large launch
+    const bool mid = !long_rows && !pf && nchunk > 1; // short rows of several chunks, large launch
     if (mid)
         nchunk = ceil_div(a.row_bytes >> 4, (int64_t)kBlock * MOE_EP_DISPATCH_VPT_MID);
     int64_t N = 0;
@@ -939,8 +942,10 @@ static hipError_t launch_dispatch_kq(const DispatchArgs &a, hipStream_t s)
         launch_dispatch_xf<KQ, L, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     else if (pf)
         launch_dispatch_xf<KQ, Sh, true, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
-    else
+    else if (mid)
         launch_dispatch_xf<KQ, Md, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
+    else
+        launch_dispatch_xf<KQ, Sh, false, false>(a, xf, g, nplane, plane_blocks, nchunk, s);
     return hipGetLastError();
 }
 
