@@ -47,6 +47,14 @@ CASES = [
                          n_lo=1, n_hi=8), 4112, 0, None),
     (dataclasses.replace(W.EP64_BF16, name="extra 64B, 16640 slots", T=260, H=64, n_lo=0, n_hi=3),
      64, 0, None),
+    # 7 KB rows in steps too large to prefetch (two vectors per lane, one
+    # workgroup per row), with the extra row loaded beside the payload or
+    # copied after it
+    (dataclasses.replace(W.EP8_BF16, name="deepseek fp8 7 KB rows, 17600 slots, extra 1 KB + eplb 64", P=16,
+                         fmt="deepseek_fp8", T=1100, H=7168, n_lo=900, n_hi=1100), 1024, 64, None),
+    (dataclasses.replace(W.EP8_BF16, name="mxfp8 7 KB rows, 17600 slots, extra 4100B copied, masked", P=16,
+                         fmt="mxfp8", T=1100, H=7168, n_lo=900, n_hi=1100), 4100, 0,
+     [0, 3, 5, 6, 9, 12, 15]),
 ]
 
 
