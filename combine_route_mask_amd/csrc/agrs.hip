@@ -4,9 +4,10 @@
 // per-rank sizes; combine reduce-scatters the hidden rows with the same
 // sizes) between P virtual ranks on one GPU.
 //
-// One workgroup per global row j of the concatenation.  All-gatherv reads
-// the row once and writes it to all P ranks; reduce-scatterv reads row j
-// of every rank's partial, sums in fp32 and writes the owning rank's row.
+// All-gatherv: one workgroup per global row j of the concatenation reads
+// the row once and writes it to all P ranks.  Reduce-scatterv: one
+// workgroup per piece of row j reads that piece of every rank's partial,
+// sums in fp32 and writes it to the owning rank's row.
 #include "formats.h"
 #include "moe_ep_internal.h"
 
@@ -76,21 +77,30 @@ __global__ __launch_bounds__(kBlock) void allgatherv_kernel(AllGatherArgs a, int
 #ifndef MOE_EP_RS_VPT
 #define MOE_EP_RS_VPT 1    // 16-byte vectors per lane per row chunk
 #endif
+// Threads per reduce-scatterv workgroup.  Each item is then one 1 KB piece
+// of a row (one vector per lane), so a workgroup's single store follows its
+// loads at once and the stores reach HBM as a dense front among the reads
+// (as in the BF16 combine).  P16 AgRs workload, same buffers, two
+// processes: 64 -> 166.0-166.3 us, 128 -> 167.0, 256 -> 170.8-171.6;
+// 128 threads with 8 ranks in flight 169.8-170.1.
+#ifndef MOE_EP_RS_BLOCK
+#define MOE_EP_RS_BLOCK 64
+#endif
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Item (global row j, chunk c): each lane owns VPT 16-byte vectors of the
-// output row and sums, in fp32 and ascending rank order, those vectors of
-// row j of every rank's partial, with the loads of G ranks in flight at
-// once; the owner of row j keeps the bf16 result.
-template <int VPT, int G>
-__global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterArgs a, int64_t rows,
-                                                                 int64_t nchunk)
+// Item (global row j, chunk c of BS * VPT vectors): each lane owns VPT
+// 16-byte vectors of the output row and sums, in fp32 and ascending rank
+// order, those vectors of row j of every rank's partial, with the loads of G
+// ranks in flight at once; the owner of row j keeps the bf16 result.
+template <int BS, int VPT, int G>
+__global__ __launch_bounds__(BS) void reduce_scatterv_kernel(ReduceScatterArgs a, int64_t rows,
+                                                             int64_t nchunk)
 {
     const int64_t nvec = a.H >> 3;
     for (int64_t w = blockIdx.x; w < rows * nchunk; w += gridDim.x) {
         const int64_t j = w / nchunk, c = w % nchunk;
-        const int64_t i0 = c * (kBlock * VPT) + threadIdx.x;
+        const int64_t i0 = c * (BS * VPT) + threadIdx.x;
         if (i0 >= nvec)
             continue;
         const int r = segment_of(a.off, a.P, j);
@@ -98,7 +108,7 @@ __global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterAr
         bool in[VPT];
 #pragma unroll
         for (int u = 0; u < VPT; ++u)
-            in[u] = i0 + u * kBlock < nvec;
+            in[u] = i0 + u * BS < nvec;
         float acc[VPT][8];
 #pragma unroll
         for (int u = 0; u < VPT; ++u)
@@ -113,7 +123,7 @@ __global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterAr
                 for (int u = 0; u < VPT; ++u)
                     if (q0 + g < a.P && in[u])
                         v[g][u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(
-                            a.in + (int64_t)(q0 + g) * a.in_stride + j * a.H + (i0 + u * kBlock) * 8));
+                            a.in + (int64_t)(q0 + g) * a.in_stride + j * a.H + (i0 + u * BS) * 8));
 #pragma unroll
             for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kBlock) void reduce_scatterv_kernel(ReduceScatterAr
                 o[e] = pack_bf16x2(acc[u][2 * e], acc[u][2 * e + 1]);
             // the output is not read again here: keep it out of the caches
             __builtin_nontemporal_store(o, reinterpret_cast<u32x4 *>(a.out + (int64_t)r * a.out_stride +
-                                                                    i * a.H + (i0 + u * kBlock) * 8));
+                                                                    i * a.H + (i0 + u * BS) * 8));
         }
     }
 }
@@ -159,9 +169,10 @@ hipError_t launch_allgatherv(const AllGatherArgs &a, int64_t rows, hipStream_t s
 
 hipError_t launch_reduce_scatterv(const ReduceScatterArgs &a, int64_t rows, hipStream_t s)
 {
-    const int64_t nchunk = ((a.H >> 3) + kBlock * MOE_EP_RS_VPT - 1) / (kBlock * MOE_EP_RS_VPT);
-    hipLaunchKernelGGL((reduce_scatterv_kernel<MOE_EP_RS_VPT, MOE_EP_RS_GATHER>),
-                       dim3(grid_for(rows * nchunk)), dim3(kBlock), 0, s, a, rows, nchunk);
+    constexpr int BS = MOE_EP_RS_BLOCK;
+    const int64_t nchunk = ((a.H >> 3) + BS * MOE_EP_RS_VPT - 1) / (BS * MOE_EP_RS_VPT);
+    hipLaunchKernelGGL((reduce_scatterv_kernel<BS, MOE_EP_RS_VPT, MOE_EP_RS_GATHER>),
+                       dim3(grid_for(rows * nchunk)), dim3(BS), 0, s, a, rows, nchunk);
     return hipGetLastError();
 }
 
