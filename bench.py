@@ -27,7 +27,9 @@ line:
                without stores, whole-buffer fill and read), timed like the
                step's launches: what its routing work costs over them
   also         the other workloads (--also), warm, or cold with a '-cold'
-               suffix; by default EP64 warm, EP8 warm and cold, EP64 NVFP4,
+               suffix, each with its kernels' counted bytes per launch
+               ("traffic", from the committed counter summaries, null where
+               none matches the current source); by default EP64 warm, EP8 warm and cold, EP64 NVFP4,
                the MXFP8 workload with FP8 combine, EP64 DeepSeekFp8, EP64
                NVFP4 with 1 KB router logits per token and 256 EPLB
                statistics per rank, EP64 with 48 of 64 ranks taking part,
@@ -103,6 +105,20 @@ def measured_traffic(kernel: str, workload: str, config: str, instance=None):
                 (instance is None or r.get("instance") == instance) and r.get("source_digest") == digest:
             return r["hbm_bytes_per_launch"]
     return None
+
+
+def step_traffic(w, config: str) -> dict:
+    """Counted HBM bytes per launch of each kernel of a step of workload w
+    from its committed counter summary (None where there is none or the
+    source has changed since)."""
+    if config == "agrs":
+        kernels = {"allgatherv": "allgatherv_kernel", "reduce_scatterv": "reduce_scatterv_kernel"}
+    elif w.combine == "fp8":
+        kernels = {"dispatch": "dispatch_kernel", "combine_quant": "combine_fp8_quant_kernel",
+                   "combine_gather": "combine_fp8_gather_kernel"}
+    else:
+        kernels = {"dispatch": "dispatch_kernel", "combine": "combine_bf16_kernel"}
+    return {k: measured_traffic(kern, w.name, config) for k, kern in kernels.items()}
 
 
 def pmc_summary(fetch_csv: str, write_csv: str, out_path: str, workload: str, config: str = "ep8"):
@@ -947,6 +963,7 @@ def main():
     m = measure(setup, args.steps, args.warmup, flush_bytes=(1 << 30) if cold else 0,
                 graphs=not args.no_graph)
     res, b = summarize(setup, m)
+    res["traffic"] = step_traffic(w, args.config)
     ref_kernels = None
     if not args.no_reference_kernels:
         print(f"[bench] reference kernels on the {w.name} buffers", file=sys.stderr, flush=True)
@@ -983,6 +1000,7 @@ def main():
                          flush_bytes=(1 << 30) if c else 0, graphs=not args.no_graph)
             ra, _ = summarize(sa, ma)
             ra["cache"] = "cold" if c else "warm"
+            ra["traffic"] = step_traffic(wa, base)
             if not c and base in ("ep8", "ep8-mxfp8"):
                 ra["note"] = ("warm: the step's inputs partly stay in the 256 MB last-level cache "
                               "between steps, so this is not an HBM-bound figure")

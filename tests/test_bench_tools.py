@@ -181,6 +181,26 @@ def test_pmc_table_phases_and_ratios(tmp_path):
     assert d2[3] == "1" and d2[-2] == "0.5" and d2[-1] == "3"
 
 
+def test_step_traffic_per_kernel(tmp_path, monkeypatch):
+    """Each kernel of a step gets its counted bytes from the workload's
+    summary; a kernel without a row (or with a stale digest) gets None."""
+    out = tmp_path / "s.txt"
+    rows = [{"kernel": "dispatch_kernel", "instance": "dispatch_kernel<2, 4, false, false, false>", "workload": "wl",
+             "hbm_bytes_per_launch": 11, "source_digest": bench.source_digest()},
+            {"kernel": "combine_bf16_kernel", "instance": "combine_bf16_kernel<128, 1, 4, false, true>",
+             "workload": "wl", "hbm_bytes_per_launch": 22, "source_digest": "stale"},
+            {"kernel": "combine_fp8_quant_kernel", "instance": "q", "workload": "wl", "hbm_bytes_per_launch": 33,
+             "source_digest": bench.source_digest()}]
+    out.write_text("# header\n" + "\n".join(json.dumps(r) for r in rows) + "\n")
+    monkeypatch.setattr(bench, "traffic_summary_path", lambda config: str(out))
+    import dataclasses
+    w = dataclasses.replace(bench.WORKLOADS["ep8"], name="wl")
+    assert bench.step_traffic(w, "x") == {"dispatch": 11, "combine": None}
+    wf = dataclasses.replace(bench.WORKLOADS["ep8-mxfp8"], name="wl")
+    assert bench.step_traffic(wf, "x") == {"dispatch": 11, "combine_quant": 33, "combine_gather": None}
+    assert set(bench.step_traffic(bench.WORKLOADS["agrs"], "agrs")) == {"allgatherv", "reduce_scatterv"}
+
+
 def test_also_plan_cache_states():
     """--also entries are warm unless suffixed '-cold'; the headline in its own
     cache state is not repeated; warm and cold runs of one workload share one
