@@ -1,6 +1,8 @@
 """Build the gfx950 HIP libraries in-tree with hipcc: ``libmoe_ep.so`` (the
 exchange behind include/moe_ep.h) and ``libmoe_ep_ceilings.so`` (the
-benchmark's plain reference kernels)."""
+benchmark's plain reference kernels); then, with the host C compiler, the
+plain C example that uses the exchange through its C ABI only
+(``_build/moe_ep_example``)."""
 from __future__ import annotations
 
 import os
@@ -16,6 +18,9 @@ SOURCES = ["exchange.hip", "agrs.hip", "api.cpp"]
 # reference kernels of the benchmark (measurement only; the exchange never calls them)
 CEILINGS_LIB = os.path.join(HERE, "libmoe_ep_ceilings.so")
 CEILINGS_SOURCES = ["ceilings.hip"]
+# a C99 program over the C ABI alone (host code; links libmoe_ep.so and the HIP runtime)
+EXAMPLE_SOURCE = os.path.join(HERE, "examples", "moe_ep_example.c")
+EXAMPLE = os.path.join(HERE, "_build", "moe_ep_example")
 
 # Packed-FP32 instructions are disabled for all device code.
 HIPCC_FLAGS = [
@@ -44,11 +49,40 @@ def _compile(out: str, sources, verbose: bool) -> str:
     return out
 
 
+def rocm_path() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def build_example(verbose: bool = False, out: str = EXAMPLE) -> str:
+    """Compile the C example as C99 against include/moe_ep.h, linked to the
+    in-tree libmoe_ep.so (found through its rpath) and the HIP runtime."""
+    cc = os.environ.get("CC") or shutil.which("gcc") or shutil.which("cc")
+    if not cc:
+        raise RuntimeError("no host C compiler found for the C example")
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    tmp = out + ".tmp%d" % os.getpid()
+    rocm = rocm_path()
+    cmd = [cc, "-std=c99", "-O2", "-Wall", "-Wextra", "-Werror", "-D__HIP_PLATFORM_AMD__",
+           "-I", INCLUDE, "-I", os.path.join(rocm, "include"), "-o", tmp, EXAMPLE_SOURCE,
+           "-L", HERE, "-lmoe_ep", "-L", os.path.join(rocm, "lib"), "-lamdhip64", "-lm",
+           "-Wl,-rpath,$ORIGIN/..:" + HERE, "-Wl,-rpath," + os.path.join(rocm, "lib")]
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("C example build failed:\n" + res.stdout + res.stderr)
+    os.replace(tmp, out)
+    return out
+
+
 def build(verbose: bool = False) -> str:
-    """Compile the exchange library libmoe_ep.so and the benchmark's
-    reference-kernel library libmoe_ep_ceilings.so (always rebuilds)."""
+    """Compile the exchange library libmoe_ep.so, the benchmark's
+    reference-kernel library libmoe_ep_ceilings.so and the C example
+    (always rebuilds)."""
     _compile(CEILINGS_LIB, CEILINGS_SOURCES, verbose)
-    return _compile(LIB, SOURCES, verbose)
+    lib = _compile(LIB, SOURCES, verbose)
+    build_example(verbose)
+    return lib
 
 
 if __name__ == "__main__":
