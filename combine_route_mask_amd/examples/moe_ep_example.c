@@ -15,6 +15,15 @@
  * its top-k weights, within the bf16 rounding of the expert rows and of the
  * result.  Rows past each rank's token count must stay as they were.
  *
+ * Then the all-gatherv / reduce-scatterv pair (vLLM AgRsAll2AllManager:
+ * dispatch gathers the hidden rows and top-k ids of every rank along dim 0
+ * with per-rank sizes, combine reduce-scatters hidden rows with the same
+ * sizes) on the same token rows, sizes n[s]: every rank must receive the
+ * concatenation of all ranks' rows and ids byte for byte, and with rank q's
+ * partial set to (q + 1) times the gathered rows, rank r's result must be,
+ * bit for bit, the fp32 sum over q in ascending order of those partials,
+ * rounded to bf16.
+ *
  * Prints "ok" and exits 0 when every check holds; exits 1 on a failed
  * check, 2 when no gfx950 device is current, 3 when a call fails.
  */
@@ -194,6 +203,67 @@ int main(void)
                 tokens += h == 0;
             }
     CHECK_EP(moe_ep_destroy(ex));
+
+    /* all-gatherv of the hidden rows and the ids, sizes n[s] */
+    int32_t off[P + 1];
+    off[0] = 0;
+    for (int s = 0; s < P; ++s)
+        off[s + 1] = off[s] + n[s];
+    const int R = off[P];
+    void *d_gh, *d_gi, *d_part, *d_rs;
+    CHECK_HIP(hipMalloc(&d_gh, (size_t)P * R * H * 2));
+    CHECK_HIP(hipMalloc(&d_gi, (size_t)P * R * K * 4));
+    CHECK_HIP(hipMalloc(&d_part, (size_t)P * R * H * 2));
+    CHECK_HIP(hipMalloc(&d_rs, (size_t)P * T * H * 2));
+    moe_ep_plane planes[2] = {
+        {d_hidden, (int64_t)T * H * 2, d_gh, (int64_t)R * H * 2, (int64_t)H * 2},
+        {d_ids, (int64_t)T * K * 4, d_gi, (int64_t)R * K * 4, (int64_t)K * 4},
+    };
+    CHECK_EP(moe_ep_allgatherv(P, n, 2, planes, NULL));
+    uint16_t *gh = (uint16_t *)malloc((size_t)P * R * H * 2);
+    int32_t *gi = (int32_t *)malloc((size_t)P * R * K * 4);
+    uint16_t *part = (uint16_t *)malloc((size_t)P * R * H * 2);
+    static uint16_t rs[P][T][H];
+    if (!gh || !gi || !part)
+        return 3;
+    CHECK_HIP(hipMemcpy(gh, d_gh, (size_t)P * R * H * 2, hipMemcpyDeviceToHost));
+    CHECK_HIP(hipMemcpy(gi, d_gi, (size_t)P * R * K * 4, hipMemcpyDeviceToHost));
+    for (int r = 0; r < P; ++r)
+        for (int s = 0; s < P; ++s)
+            for (int t = 0; t < n[s]; ++t) {
+                const size_t j = (size_t)r * R + off[s] + t;
+                bad += memcmp(gh + j * H, hidden[s][t], (size_t)H * 2) != 0;
+                bad += memcmp(gi + j * K, ids[s][t], (size_t)K * 4) != 0;
+            }
+    const int gather_bad = bad;
+
+    /* reduce-scatterv: rank q's partial is (q + 1) times the gathered rows */
+    for (int q = 0; q < P; ++q)
+        for (size_t e = 0; e < (size_t)R * H; ++e)
+            part[(size_t)q * R * H + e] = f32_to_bf16((float)(q + 1) * bf16_to_f32(gh[e]));
+    CHECK_HIP(hipMemcpy(d_part, part, (size_t)P * R * H * 2, hipMemcpyHostToDevice));
+    CHECK_HIP(hipMemset(d_rs, 0x5A, (size_t)P * T * H * 2));
+    CHECK_EP(moe_ep_reduce_scatterv(P, n, H, d_part, (int64_t)R * H * 2, d_rs, (int64_t)T * H * 2, NULL));
+    CHECK_HIP(hipMemcpy(rs, d_rs, sizeof rs, hipMemcpyDeviceToHost));
+    for (int r = 0; r < P; ++r)
+        for (int t = 0; t < T; ++t)
+            for (int h = 0; h < H; ++h) {
+                if (t >= n[r]) {
+                    bad += rs[r][t][h] != 0x5A5A;
+                    continue;
+                }
+                float acc = 0.0f;
+                for (int q = 0; q < P; ++q)
+                    acc += bf16_to_f32(part[((size_t)q * R + off[r] + t) * H + h]);
+                bad += rs[r][t][h] != f32_to_bf16(acc);
+            }
+    (void)hipFree(d_gh);
+    (void)hipFree(d_gi);
+    (void)hipFree(d_part);
+    (void)hipFree(d_rs);
+    free(gh);
+    free(gi);
+    free(part);
     (void)hipFree(d_ws);
     (void)hipFree(d_hidden);
     (void)hipFree(d_ids);
@@ -203,10 +273,11 @@ int main(void)
     free(ws);
     free(eo);
     if (bad) {
-        fprintf(stderr, "%d elements outside the bound\n", bad);
+        fprintf(stderr, "%d checks failed (%d in the all-gatherv)\n", bad, gather_bad);
         return 1;
     }
-    printf("ok: %d tokens, %d (token, rank) rows, every token back as its row times its weight sum\n", tokens,
-           received);
+    printf("ok: %d tokens, %d (token, rank) rows, every token back as its row times its weight sum; "
+           "%d rows gathered to %d ranks and reduce-scattered bit-exact\n",
+           tokens, received, R, P);
     return 0;
 }

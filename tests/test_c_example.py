@@ -5,7 +5,10 @@ runtime, and refuses to run without a gfx950 device.  On the GPU it runs a
 small dispatch, plays identity experts on the host from the returned id
 and weight planes, combines, and checks that every token comes back as its
 row times the sum of its top-k weights (the combine's contract) with the
-rows past each rank's token count untouched."""
+rows past each rank's token count untouched; then it all-gathers the token
+rows and ids (every rank gets every rank's rows, byte for byte) and
+reduce-scatters (q + 1)-scaled copies of them (each result row equal, bit
+for bit, to the fp32 ascending-rank sum rounded to bf16)."""
 import os
 import subprocess
 
@@ -38,5 +41,5 @@ def test_example_runs_a_step_through_the_c_abi():
     exe = build.EXAMPLE if os.path.exists(build.EXAMPLE) else build.build_example()
     res = subprocess.run([exe], capture_output=True, text=True, timeout=120)
     assert res.returncode == 0, res.stdout + res.stderr
-    assert res.stdout.startswith("ok:"), res.stdout
+    assert res.stdout.startswith("ok:") and "reduce-scattered bit-exact" in res.stdout, res.stdout
     print(res.stdout.strip(), flush=True)
